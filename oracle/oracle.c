@@ -1,0 +1,518 @@
+/*
+ * CPU oracle for the FP4 routed mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file: only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark use it. It shares no code, header, table or constant generator
+ * with the HIP library; both sides take their inputs from the seeded generators
+ * and nothing else.
+ *
+ * What it computes (the layer the pages centre on: "FP4 routed
+ * mixture-of-experts computation" with "packed FP4 weights" and "INT8
+ * activation quantization", abstract of "DeepSeek-V4-Flash on AMD gfx90a:
+ * Correctness Recovery and Inference Performance Engineering"; 256 routed
+ * experts with 6 active per token, "What we set out to do" in "DeepSeek V4
+ * Flash on 8x AMD gfx1201: packaged TP=8 deployment"):
+ *
+ *   1. router logits  l[t,e] = <x[t,:], Wr[e,:]> (+ b[e])            fp32
+ *   2. scores s = sigmoid(l); the k largest (ties -> lower expert);
+ *      weights w_j = s_j / sum_j s_j                                     fp32
+ *   3. expert sort: stable counting sort of the T*k (token, slot) pairs by
+ *      expert, each expert segment padded to a multiple of block_m
+ *   4. activation quantization: per-row symmetric int8, or MXFP4 (E2M1
+ *      codes with one E8M0 scale per 32 along K, OCP Microscaling v1.0)
+ *   5. gate/up GEMM against packed E2M1 weights with block-32 E8M0 scales,
+ *      a = silu(g) * u, requantized like step 4
+ *   6. down GEMM against W2
+ *   7. out[t] = sum_j w_j * y[pair(t, j)]
+ *
+ * Floating point is fp32 where the layer fixes fp32 (router, accumulation
+ * over scale blocks, activation), with every reduction in one written-down
+ * order so that a second implementation can reproduce the bits. Block sums
+ * of code products are exact integers. The readings taken where the pages
+ * leave a step open are stated beside each function.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * -ffp-contract=off matters: every fused multiply-add below is written as
+ * fmaf() and every other product/sum must round on its own.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Formats (OCP Microscaling Formats v1.0: E2M1 element, E8M0 scale)        */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent field 0 is subnormal: value = m * 2^(1-1) * 0.5. */
+float or_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    float mag = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0: an unsigned biased exponent, value 2^(b-127); 0xFF encodes NaN. */
+float or_e8m0_value(int b)
+{
+    if (b == 255) return NAN;
+    return ldexpf(1.0f, b - 127);
+}
+
+/* Twice an E2M1 value is an integer in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}. */
+static int twice_e2m1(int code) { return (int)(2.0f * or_e2m1_value(code)); }
+
+static int nibble(const uint8_t* row, int k) { return (row[k >> 1] >> ((k & 1) * 4)) & 15; }
+
+/* ------------------------------------------------------------------------ */
+/* exp and sigmoid in fp32, from the mathematics                            */
+/* ------------------------------------------------------------------------ */
+/* exp(z) = 2^n * exp(r), n = rint(z * log2 e), r = z - n ln2 by a two-term
+ * Cody-Waite split of ln 2 (the high part keeps 15 significant bits so n*hi
+ * is exact for |n| <= 256), exp(r) by its Taylor series to degree 7 in
+ * Horner form with fused multiply-adds, then an exact power-of-two scaling.
+ * Only IEEE operations with one rounding each are used (mul, fma, rint,
+ * ldexp, add, div), so any conforming fp32 implementation gets the same bits.
+ * The Taylor remainder on |r| <= ln2/2 is below 0.1 ulp. */
+#define OR_LOG2E 0x1.715476p+0f   /* fp32(log2 e) */
+#define OR_LN2_HI 0x1.62e4p-1f    /* ln 2 truncated to 15 significant bits */
+#define OR_LN2_LO 0x1.7f7d1cp-20f /* fp32(ln 2 - OR_LN2_HI) */
+#define OR_EXP_HI 0x1.62e42ep+6f  /* largest z with finite fp32 exp(z) */
+#define OR_EXP_LO (-0x1.9fe36ap+6f) /* fp32 just below ln(2^-150): exp rounds to 0 */
+
+float or_expf(float z)
+{
+    if (z != z) return z;
+    if (z > OR_EXP_HI) return INFINITY;
+    if (z < OR_EXP_LO) return 0.0f;
+    float n = rintf(z * OR_LOG2E);
+    float r = fmaf(-n, OR_LN2_HI, z);
+    r = fmaf(-n, OR_LN2_LO, r);
+    /* 1/k! for k = 7..0 */
+    float p = 0x1.a01a02p-13f;        /* 1/5040 */
+    p = fmaf(p, r, 0x1.6c16c2p-10f);  /* 1/720 */
+    p = fmaf(p, r, 0x1.111112p-7f);   /* 1/120 */
+    p = fmaf(p, r, 0x1.555556p-5f);   /* 1/24 */
+    p = fmaf(p, r, 0x1.555556p-3f);   /* 1/6 */
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)n);
+}
+
+float or_sigmoidf(float z) { return 1.0f / (1.0f + or_expf(-z)); }
+
+/* ------------------------------------------------------------------------ */
+/* Ordered fp32 dot product                                                  */
+/* ------------------------------------------------------------------------ */
+/* Reading of the reduction order (the pages give none; bit-exact routing
+ * needs one): split the length-H vectors into 64 contiguous chunks of
+ * L = H/64; each chunk is a chain p = fma(a_i, b_i, p) from p = 0 over
+ * ascending i; the 64 partials are then summed as a perfect pairwise tree in
+ * index order (level 1: p0+p1, p2+p3, ...; six levels). */
+static float ordered_dot(int H, const float* a, const float* b)
+{
+    float part[64];
+    int L = H / 64;
+    for (int c = 0; c < 64; ++c) {
+        float p = 0.0f;
+        for (int i = 0; i < L; ++i) p = fmaf(a[c * L + i], b[c * L + i], p);
+        part[c] = p;
+    }
+    for (int width = 64; width > 1; width /= 2)
+        for (int j = 0; j < width / 2; ++j) part[j] = part[2 * j] + part[2 * j + 1];
+    return part[0];
+}
+
+/* x arrives as fp32 or as bf16 bit patterns; bf16 -> fp32 is exact. */
+void or_x_to_f32(int T, int H, int x_dtype, const void* x, float* xf)
+{
+    if (x_dtype == 0) {
+        memcpy(xf, x, (size_t)T * H * sizeof(float));
+        return;
+    }
+    const uint16_t* xb = (const uint16_t*)x;
+    for (size_t i = 0; i < (size_t)T * H; ++i) {
+        uint32_t u = (uint32_t)xb[i] << 16;
+        memcpy(&xf[i], &u, 4);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router: logits, sigmoid, top-k, renormalization                          */
+/* ------------------------------------------------------------------------ */
+/* Router logits on unquantized x (fp32). The optional bias is added to the
+ * finished dot product as one fp32 add, before the sigmoid, so it moves both
+ * the selection and the weights. */
+void or_router_logits(int T, int H, int E, const float* xf, const float* wr,
+                      const float* bias, float* logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            float l = ordered_dot(H, xf + (size_t)t * H, wr + (size_t)e * H);
+            if (bias) l = l + bias[e];
+            logits[(size_t)t * E + e] = l;
+        }
+}
+
+/* Sigmoid scores; pick the k largest scores, ties to the lower expert index,
+ * slot j holding the j-th pick; renormalize: S = ((s_0 + s_1) + s_2) + ...
+ * in slot order and w_j = s_j / S (w_j = 1/k if S == 0). No group-limited
+ * routing and a routed scaling factor of 1. */
+void or_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w, float* scores_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        float* s = (float*)malloc((size_t)E * sizeof(float));
+        char* taken = (char*)calloc((size_t)E, 1);
+        for (int e = 0; e < E; ++e) s[e] = or_sigmoidf(logits[(size_t)t * E + e]);
+        if (scores_out) memcpy(scores_out + (size_t)t * E, s, (size_t)E * sizeof(float));
+        float S = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || s[e] > s[best])) best = e;
+            taken[best] = 1;
+            ids[(size_t)t * k + j] = best;
+            S = S + s[best];
+        }
+        for (int j = 0; j < k; ++j) {
+            float sj = s[ids[(size_t)t * k + j]];
+            w[(size_t)t * k + j] = (S == 0.0f) ? 1.0f / (float)k : sj / S;
+        }
+        free(s);
+        free(taken);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert sort ("retuned expert sorting", abstract of the gfx90a paper)     */
+/* ------------------------------------------------------------------------ */
+/* Pairs are numbered i = t*k + j. counts[e] = pairs routed to e. Each
+ * expert's segment is padded up to a multiple of block_m; offsets[e] is the
+ * segment start (offsets[E] = padded total). sorted[p] is the pair index at
+ * padded position p (pairs of one expert in ascending i), or the sentinel P
+ * in padding. pos[i] is where pair i landed. tile_expert[q] is the expert of
+ * the q-th block of block_m positions; *n_tiles = offsets[E] / block_m.
+ * Returns the padded total. */
+int or_sort(int P, int E, int block_m, const int32_t* ids, int32_t* counts, int32_t* offsets,
+            int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles)
+{
+    for (int e = 0; e < E; ++e) counts[e] = 0;
+    for (int i = 0; i < P; ++i) counts[ids[i]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int padded = (counts[e] + block_m - 1) / block_m * block_m;
+        offsets[e + 1] = offsets[e] + padded;
+    }
+    int total = offsets[E];
+    for (int p = 0; p < total; ++p) sorted[p] = P;
+    int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    for (int i = 0; i < P; ++i) {
+        int e = ids[i];
+        int p = offsets[e] + fill[e]++;
+        sorted[p] = i;
+        pos[i] = p;
+    }
+    free(fill);
+    int nt = 0;
+    for (int e = 0; e < E; ++e)
+        for (int p = offsets[e]; p < offsets[e + 1]; p += block_m) tile_expert[nt++] = e;
+    *n_tiles = nt;
+    return total;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation quantization                                                   */
+/* ------------------------------------------------------------------------ */
+/* Symmetric int8 per row: amax = max |v|, s = amax / 127,
+ * q = clamp(rint(v / s), -127, 127) with ties to even; amax = 0 gives s = 0
+ * and q = 0. */
+void or_quant_int8(int R, int K, const float* v, int8_t* q, float* s)
+{
+    for (int r = 0; r < R; ++r) {
+        const float* row = v + (size_t)r * K;
+        float amax = 0.0f;
+        for (int i = 0; i < K; ++i) amax = fmaxf(amax, fabsf(row[i]));
+        float sc = amax / 127.0f;
+        s[r] = sc;
+        for (int i = 0; i < K; ++i) {
+            float qq = (amax == 0.0f) ? 0.0f : rintf(row[i] / sc);
+            if (qq > 127.0f) qq = 127.0f;
+            if (qq < -127.0f) qq = -127.0f;
+            q[(size_t)r * K + i] = (int8_t)qq;
+        }
+    }
+}
+
+/* Nearest E2M1 magnitude code for a >= 0, ties to the code with mantissa bit
+ * 0; everything above 6 saturates to 6. Written as a scan over the eight
+ * magnitudes, which is the definition of round-to-nearest-even on this grid. */
+static int e2m1_nearest_mag(float a)
+{
+    int best = 0;
+    float bestd = INFINITY;
+    for (int m = 0; m < 8; ++m) {
+        float d = fabsf(a - or_e2m1_value(m));
+        if (d < bestd || (d == bestd && (m & 1) == 0 && (best & 1) == 1)) {
+            best = m;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* MXFP4 per block of 32 along K (OCP MX v1.0 conversion): the shared scale
+ * exponent is floor(log2 amax) - 2 (2 = the largest E2M1 exponent), stored
+ * biased by 127 and clamped to [0, 254]; elements are scaled exactly by
+ * 2^(127 - e) and rounded to nearest-even on the E2M1 grid with saturation at
+ * 6. The code's sign bit is the sign bit of the element (so -0 may appear).
+ * A block with amax = 0 gets scale byte 0 and codes 0.
+ * codes: [R][K/2] (low nibble = even k); scales: [R][K/32]. */
+void or_quant_mxfp4(int R, int K, const float* v, uint8_t* codes, uint8_t* scales)
+{
+    memset(codes, 0, (size_t)R * K / 2);
+    for (int r = 0; r < R; ++r)
+        for (int b = 0; b < K / 32; ++b) {
+            const float* blk = v + (size_t)r * K + 32 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(blk[i]));
+            int e = 0;
+            if (amax > 0.0f) {
+                int ex;
+                frexpf(amax, &ex); /* amax = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1 */
+                e = (ex - 1) - 2 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            scales[(size_t)r * (K / 32) + b] = (uint8_t)e;
+            for (int i = 0; i < 32; ++i) {
+                int code = 0;
+                if (amax > 0.0f) {
+                    float vs = ldexpf(blk[i], 127 - e);
+                    code = e2m1_nearest_mag(fabsf(vs)) | (signbit(vs) ? 8 : 0);
+                }
+                int k = 32 * b + i;
+                codes[(size_t)r * (K / 2) + k / 2] |= (uint8_t)(code << ((k & 1) * 4));
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* One output row of a block-scaled FP4 GEMM                                 */
+/* ------------------------------------------------------------------------ */
+/* Weights W[N][K]: codes [N][K/2], E8M0 scales [N][K/32], block 32 along K.
+ * int8 activations (q, s):
+ *   isum_b = sum_{i in b} q_i * (2 c_i)                     exact int32
+ *   acc    = acc + isum_b * 2^(e_b - 128)  over ascending b  fp32
+ *   out_n  = s * acc
+ * MXFP4 activations (codes cx, scales ex):
+ *   isum_b = sum (2 cx_i)(2 cw_i);  acc = acc + isum_b * 2^(ex_b + ew_b - 256)
+ *   out_n  = acc
+ * (Each product isum_b * 2^m is exact; only the fp32 additions round.) */
+static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t* wc,
+                          const uint8_t* ws, float* out)
+{
+    for (int n = 0; n < N; ++n) {
+        const uint8_t* row = wc + (size_t)n * (K / 2);
+        float acc = 0.0f;
+        for (int b = 0; b < K / 32; ++b) {
+            int32_t isum = 0;
+            for (int i = 0; i < 32; ++i) {
+                int k = 32 * b + i;
+                isum += (int32_t)q[k] * twice_e2m1(nibble(row, k));
+            }
+            acc = acc + ldexpf((float)isum, (int)ws[(size_t)n * (K / 32) + b] - 128);
+        }
+        out[n] = s * acc;
+    }
+}
+
+static void gemm_row_mxfp4(int K, int N, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc,
+                           const uint8_t* ws, float* out)
+{
+    for (int n = 0; n < N; ++n) {
+        const uint8_t* row = wc + (size_t)n * (K / 2);
+        float acc = 0.0f;
+        for (int b = 0; b < K / 32; ++b) {
+            int32_t isum = 0;
+            for (int i = 0; i < 32; ++i) {
+                int k = 32 * b + i;
+                isum += twice_e2m1(nibble(xc, k)) * twice_e2m1(nibble(row, k));
+            }
+            int sh = (int)xs[b] + (int)ws[(size_t)n * (K / 32) + b] - 256;
+            acc = acc + ldexpf((float)isum, sh);
+        }
+        out[n] = acc;
+    }
+}
+
+/* a = (g * sigmoid(g)) * u, two fp32 multiplies in that order; g = h[0:I],
+ * u = h[I:2I] (gate rows first in W13). */
+static void silu_mul(int I, const float* h, float* a)
+{
+    for (int n = 0; n < I; ++n) {
+        float g = h[n], u = h[I + n];
+        a[n] = (g * or_sigmoidf(g)) * u;
+    }
+}
+
+/* Public single-row entry points (used by tests on intermediates). */
+void or_gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t* wc, const uint8_t* ws, float* out)
+{
+    gemm_row_int8(K, N, q, s, wc, ws, out);
+}
+void or_gemm_row_mxfp4(int K, int N, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc,
+                       const uint8_t* ws, float* out)
+{
+    gemm_row_mxfp4(K, N, xc, xs, wc, ws, out);
+}
+void or_silu_mul(int I, const float* h, float* a) { silu_mul(I, h, a); }
+
+/* ------------------------------------------------------------------------ */
+/* The whole layer for a list of tokens                                      */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t T, H, I, E, top_k, x_dtype, act_mode;
+} or_config;
+
+/* Every output of the layer depends only on its own token, so the oracle
+ * computes any subset of tokens exactly as it would inside the whole batch.
+ * x: [T][H] (fp32 or bf16 bits) of the tokens to compute. Weights are given
+ * per expert (arrays of E pointers, canonical layout: W13 [2I][H/2] codes,
+ * [2I][H/32] scales; W2 [H][I/2], [H][I/32]); a NULL entry is allowed for an
+ * expert that no token selects. Optional outputs (NULL to skip), pair p =
+ * t*k + j: ids/w [T][k]; xq (int8 [T][H] or codes [T][H/2]) and xs (fp32 [T]
+ * or bytes [T][H/32]); h [P][2I]; aq/as like xq/xs with K = I; y [P][H].
+ * Returns 0, or -1 if a needed expert pointer is NULL. */
+int or_moe_layer(const or_config* c, const void* x, const float* wr, const float* bias,
+                 const uint8_t* const* w13, const uint8_t* const* w13s,
+                 const uint8_t* const* w2, const uint8_t* const* w2s,
+                 float* out, int32_t* ids_out, float* w_out,
+                 void* xq_out, void* xs_out, float* h_out, void* aq_out, void* as_out, float* y_out)
+{
+    const int T = c->T, H = c->H, I = c->I, E = c->E, k = c->top_k;
+    const int mx = c->act_mode == 1;
+    const int P = T * k;
+    float* xf = (float*)malloc((size_t)T * H * sizeof(float));
+    float* logits = (float*)malloc((size_t)T * E * sizeof(float));
+    int32_t* ids = (int32_t*)malloc((size_t)P * sizeof(int32_t));
+    float* wts = (float*)malloc((size_t)P * sizeof(float));
+    or_x_to_f32(T, H, c->x_dtype, x, xf);
+    or_router_logits(T, H, E, xf, wr, bias, logits);
+    or_topk(T, E, k, logits, ids, wts, NULL);
+    for (int p = 0; p < P; ++p)
+        if (!w13[ids[p]] || !w13s[ids[p]] || !w2[ids[p]] || !w2s[ids[p]]) {
+            free(xf); free(logits); free(ids); free(wts);
+            return -1;
+        }
+
+    /* activation quantization of x (per token) */
+    size_t xq_row = mx ? (size_t)H / 2 : (size_t)H;
+    size_t xs_row = mx ? (size_t)H / 32 : sizeof(float);
+    uint8_t* xq = (uint8_t*)malloc((size_t)T * xq_row);
+    uint8_t* xs = (uint8_t*)malloc((size_t)T * xs_row);
+    if (mx) or_quant_mxfp4(T, H, xf, xq, xs);
+    else or_quant_int8(T, H, xf, (int8_t*)xq, (float*)xs);
+    if (xq_out) memcpy(xq_out, xq, (size_t)T * xq_row);
+    if (xs_out) memcpy(xs_out, xs, (size_t)T * xs_row);
+
+    size_t aq_row = mx ? (size_t)I / 2 : (size_t)I;
+    size_t as_row = mx ? (size_t)I / 32 : sizeof(float);
+    float* y = (float*)malloc((size_t)P * H * sizeof(float));
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int p = 0; p < P; ++p) {
+        int t = p / k, e = ids[p];
+        float* h = (float*)malloc((size_t)2 * I * sizeof(float));
+        float* a = (float*)malloc((size_t)I * sizeof(float));
+        uint8_t* aq = (uint8_t*)malloc(aq_row);
+        uint8_t* asp = (uint8_t*)malloc(as_row);
+        if (mx)
+            gemm_row_mxfp4(H, 2 * I, xq + (size_t)t * xq_row, xs + (size_t)t * xs_row, w13[e], w13s[e], h);
+        else
+            gemm_row_int8(H, 2 * I, (const int8_t*)(xq + (size_t)t * xq_row),
+                          ((const float*)xs)[t], w13[e], w13s[e], h);
+        silu_mul(I, h, a);
+        if (mx) or_quant_mxfp4(1, I, a, aq, asp);
+        else or_quant_int8(1, I, a, (int8_t*)aq, (float*)asp);
+        if (mx)
+            gemm_row_mxfp4(I, H, aq, asp, w2[e], w2s[e], y + (size_t)p * H);
+        else
+            gemm_row_int8(I, H, (const int8_t*)aq, *(const float*)asp, w2[e], w2s[e], y + (size_t)p * H);
+        if (h_out) memcpy(h_out + (size_t)p * 2 * I, h, (size_t)2 * I * sizeof(float));
+        if (aq_out) memcpy((uint8_t*)aq_out + (size_t)p * aq_row, aq, aq_row);
+        if (as_out) memcpy((uint8_t*)as_out + (size_t)p * as_row, asp, as_row);
+        free(asp); free(h); free(a); free(aq);
+    }
+
+    /* combine: acc = fma(w_j, y_j, acc) over ascending slots, from 0 */
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < H; ++n) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j)
+                acc = fmaf(wts[(size_t)t * k + j], y[((size_t)t * k + j) * H + n], acc);
+            out[(size_t)t * H + n] = acc;
+        }
+
+    if (ids_out) memcpy(ids_out, ids, (size_t)P * sizeof(int32_t));
+    if (w_out) memcpy(w_out, wts, (size_t)P * sizeof(float));
+    if (y_out) memcpy(y_out, y, (size_t)P * H * sizeof(float));
+    free(xf); free(logits); free(ids); free(wts); free(xq); free(xs); free(y);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm for the stacked-layer residual stream                             */
+/* ------------------------------------------------------------------------ */
+/* Unit-gain RMSNorm between stacked layers (x_{l+1} = x_l + moe(rmsnorm(x_l))):
+ * ss = ordered_dot(x, x) in the same chunked order as the router,
+ * r = sqrt(ss / H + 1e-6) with IEEE sqrt and division, out = x / r. */
+void or_rmsnorm(int T, int H, const float* x, float* out)
+{
+    for (int t = 0; t < T; ++t) {
+        const float* row = x + (size_t)t * H;
+        float ss = ordered_dot(H, row, row);
+        float r = sqrtf(ss / (float)H + 1e-6f);
+        for (int i = 0; i < H; ++i) out[(size_t)t * H + i] = row[i] / r;
+    }
+}
+
+int or_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Array forms for the tests. */
+void or_expf_n(int n, const float* z, float* out)
+{
+    for (int i = 0; i < n; ++i) out[i] = or_expf(z[i]);
+}
+void or_sigmoidf_n(int n, const float* z, float* out)
+{
+    for (int i = 0; i < n; ++i) out[i] = or_sigmoidf(z[i]);
+}
+void or_e2m1_table(float* out16)
+{
+    for (int c = 0; c < 16; ++c) out16[c] = or_e2m1_value(c);
+}

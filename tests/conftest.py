@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size CPU oracle work")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests run in file order; nothing to reorder. Kept for the marker only.
+    return None
+
+
+@pytest.fixture(scope="session")
+def oracle():
+    import oracle as _o
+    _o.lib()
+    return _o
