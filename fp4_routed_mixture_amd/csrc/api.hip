@@ -1,0 +1,321 @@
+// C ABI of the routed-MoE layer: argument checks, workspace plan, launches.
+// Everything here runs on the host; every computation runs in the kernels.
+#include <string.h>
+
+#include "../../include/fp4moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+#define MOE_TRY(call)                            \
+  do {                                           \
+    hipError_t e_ = (call);                      \
+    if (e_ != hipSuccess) return hip_fail(e_);   \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t up256(size_t n) { return (n + 255) / 256 * 256; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_shape(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->x_dtype != MOE_X_F32 && c->x_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->act_mode != MOE_ACT_INT8 && c->act_mode != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->T > (1 << 20)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->H < 256 || c->H > 16384 || c->H % 256) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->I < 128 || c->I > 16384 || c->I % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->E < 1 || c->E > 1024) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->E) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+// Workspace plan of one layer call.
+struct Plan {
+  int block_m, P, cap, max_tiles;
+  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, a, aq, as, y, total;
+};
+
+Plan make_plan(const moe_config* c) {
+  Plan p;
+  const int T = c->T, H = c->H, I = c->I, E = c->E, k = c->top_k;
+  const bool mx = c->act_mode == MOE_ACT_MXFP4;
+  p.block_m = mx ? moe_k_prefill_block_m() : 16;
+  p.P = T * k;
+  p.cap = p.P + (E < p.P ? E : p.P) * (p.block_m - 1);
+  p.max_tiles = p.cap / p.block_m;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += up256(bytes);
+    return o;
+  };
+  p.logits = take((size_t)T * E * 4);
+  p.ids = take((size_t)p.P * 4);
+  p.w = take((size_t)p.P * 4);
+  p.xq = take(mx ? (size_t)T * H / 2 : (size_t)T * 2 * H);
+  p.xs = take(mx ? (size_t)T * H / 32 : (size_t)T * 4);
+  p.counts = take((size_t)E * 4);
+  p.offsets = take((size_t)(E + 1) * 4);
+  p.sorted = take((size_t)p.cap * 4);
+  p.pos = take((size_t)p.P * 4);
+  p.tiles = take((size_t)(p.max_tiles + 1) * 4);
+  p.ntiles = take(4);
+  p.sort_scratch = take(moe_k_sort_scratch_bytes(p.P, E));
+  p.a = take(mx ? 0 : (size_t)p.cap * I * 4);
+  p.aq = take(mx ? (size_t)p.cap * I / 2 : (size_t)p.cap * 2 * I);
+  p.as = take(mx ? (size_t)p.cap * I / 32 : (size_t)p.cap * 4);
+  p.y = take((size_t)p.P * H * 4);
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return FP4MOE_ABI_VERSION; }
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_ALIAS: return "output overlaps an input";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = make_plan(cfg).total;
+  return MOE_OK;
+}
+
+int moe_prepacked_size(int32_t which, int32_t E, int32_t N, int32_t K, size_t* code_bytes, size_t* scale_bytes) {
+  if (which != MOE_W13 && which != MOE_W2) return MOE_ERR_INVALID_ARG;
+  if (!code_bytes || !scale_bytes) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || N < 32 || K < 64 || K % 64) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (which == MOE_W13 ? (N % 64) : (N % 32)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  *code_bytes = (size_t)E * N * K / 2;
+  *scale_bytes = moe_k_packed_scale_bytes(which, E, N, K);
+  return MOE_OK;
+}
+
+int moe_prepack(int32_t which, int32_t E, int32_t N, int32_t K, const uint8_t* codes, const uint8_t* scales,
+                const int32_t* row_perm, uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  size_t cb, sb;
+  int st = moe_prepacked_size(which, E, N, K, &cb, &sb);
+  if (st) return st;
+  if (!codes || !scales || !packed_codes || !packed_scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(packed_codes) || !aligned16(packed_scales)) return MOE_ERR_ALIGNMENT;
+  if (overlaps(codes, cb, packed_codes, cb) || overlaps(scales, (size_t)E * N * K / 32, packed_scales, sb))
+    return MOE_ERR_ALIAS;
+  MOE_TRY(moe_k_pack(which, E, N, K, codes, scales, row_perm, packed_codes, packed_scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_unpack(int32_t which, int32_t E, int32_t N, int32_t K, const uint8_t* packed_codes,
+               const uint8_t* packed_scales, uint8_t* codes, uint8_t* scales, void* stream) {
+  size_t cb, sb;
+  int st = moe_prepacked_size(which, E, N, K, &cb, &sb);
+  if (st) return st;
+  if (!codes || !scales || !packed_codes || !packed_scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(packed_codes) || !aligned16(packed_scales)) return MOE_ERR_ALIGNMENT;
+  if (overlaps(codes, cb, packed_codes, cb) || overlaps(scales, (size_t)E * N * K / 32, packed_scales, sb))
+    return MOE_ERR_ALIAS;
+  MOE_TRY(moe_k_unpack(which, E, N, K, packed_codes, packed_scales, codes, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+              int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !router_w || !topk_ids || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  Plan p = make_plan(cfg);
+  if (workspace_bytes < p.logits + (size_t)cfg->T * cfg->E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = at<float>(workspace, p.logits);
+  MOE_TRY(moe_k_router_logits(cfg->x_dtype, x, router_w, router_bias, logits, cfg->T, cfg->H, cfg->E, s));
+  MOE_TRY(moe_k_topk(logits, cfg->T, cfg->E, cfg->top_k, topk_ids, topk_w, s));
+  return MOE_OK;
+}
+
+int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+             int32_t* sorted_pairs, int32_t* pair_pos, int32_t* tile_expert, int32_t* n_tiles, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (block_m < 1 || block_m > 1024) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!counts || !offsets || !tile_expert || !n_tiles) return MOE_ERR_INVALID_ARG;
+  const int P = cfg->T * cfg->top_k;
+  if (P > 0 && (!topk_ids || !sorted_pairs || !pair_pos)) return MOE_ERR_INVALID_ARG;
+  size_t scratch = moe_k_sort_scratch_bytes(P, cfg->E);
+  if (scratch && !workspace) return MOE_ERR_INVALID_ARG;
+  if (scratch && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  if (workspace_bytes < scratch) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  MOE_TRY(moe_k_sort(topk_ids, P, cfg->E, block_m, counts, offsets, sorted_pairs, pair_pos, tile_expert, n_tiles,
+                     workspace, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_quantize(const moe_config* cfg, int32_t rows, int32_t K, int32_t in_dtype, const void* v, void* q,
+                 void* scales, void* stream) {
+  if (!cfg) return MOE_ERR_INVALID_ARG;
+  if (cfg->act_mode != MOE_ACT_INT8 && cfg->act_mode != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (in_dtype != MOE_X_F32 && in_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows < 0 || K < 64 || K % 64 || K > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!v || !q || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(v) || !aligned16(q)) return MOE_ERR_ALIGNMENT;
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->act_mode == MOE_ACT_INT8)
+    MOE_TRY(moe_k_quant_int8(in_dtype, v, rows, K, 0, q, (float*)scales, nullptr, 0, nullptr, s));
+  else
+    MOE_TRY(moe_k_quant_mxfp4(in_dtype, v, rows, K, (uint8_t*)q, (uint8_t*)scales, s));
+  return MOE_OK;
+}
+
+int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                     const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                     float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !router_w || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w13_scale) || !aligned16(w2) ||
+      !aligned16(w2_scale) || !aligned16(out) || ((uintptr_t)workspace & 255))
+    return MOE_ERR_ALIGNMENT;
+  const int T = cfg->T, H = cfg->H, I = cfg->I, E = cfg->E, k = cfg->top_k;
+  const bool mx = cfg->act_mode == MOE_ACT_MXFP4;
+  const size_t xbytes = (size_t)T * H * (cfg->x_dtype == MOE_X_F32 ? 4 : 2);
+  if (overlaps(out, (size_t)T * H * 4, x, xbytes)) return MOE_ERR_ALIAS;
+  Plan p = make_plan(cfg);
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlaps(workspace, p.total, x, xbytes) || overlaps(workspace, p.total, out, (size_t)T * H * 4))
+    return MOE_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = at<float>(workspace, p.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, p.ids);
+  float* w = topk_w_out ? topk_w_out : at<float>(workspace, p.w);
+  uint8_t* xq = at<uint8_t>(workspace, p.xq);
+  void* xs = at<void>(workspace, p.xs);
+  int32_t* counts = at<int32_t>(workspace, p.counts);
+  int32_t* offsets = at<int32_t>(workspace, p.offsets);
+  int32_t* sorted = at<int32_t>(workspace, p.sorted);
+  int32_t* pos = at<int32_t>(workspace, p.pos);
+  int32_t* tiles = at<int32_t>(workspace, p.tiles);
+  int32_t* ntiles = at<int32_t>(workspace, p.ntiles);
+  void* sort_scratch = at<void>(workspace, p.sort_scratch);
+  float* a = at<float>(workspace, p.a);
+  uint8_t* aq = at<uint8_t>(workspace, p.aq);
+  void* as = at<void>(workspace, p.as);
+  float* y = at<float>(workspace, p.y);
+  const int P = p.P;
+
+  // route
+  MOE_TRY(moe_k_router_logits(cfg->x_dtype, x, router_w, router_bias, logits, T, H, E, s));
+  MOE_TRY(moe_k_topk(logits, T, E, k, ids, w, s));
+  // quantize x
+  if (mx)
+    MOE_TRY(moe_k_quant_mxfp4(cfg->x_dtype, x, T, H, xq, (uint8_t*)xs, s));
+  else
+    MOE_TRY(moe_k_quant_int8(cfg->x_dtype, x, T, H, 1, xq, (float*)xs, nullptr, 0, nullptr, s));
+  // sort
+  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
+  // expert GEMMs
+  if (mx) {
+    MOE_TRY(moe_k_prefill_gemm(1, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, ntiles, p.max_tiles, H,
+                               I / 32, k, P, 1, aq, (uint8_t*)as, nullptr, I, s));
+    MOE_TRY(moe_k_prefill_gemm(0, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
+                               H / 32, k, P, 0, nullptr, nullptr, y, H, s));
+  } else {
+    MOE_TRY(moe_k_decode_gemm(1, w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I / 32,
+                              k, P, 1, a, I, s));
+    MOE_TRY(moe_k_quant_int8(MOE_X_F32, a, p.cap, I, 1, aq, (float*)as, sorted, P, offsets + E, s));
+    MOE_TRY(moe_k_decode_gemm(0, w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, I, H / 32,
+                              k, P, 0, y, H, s));
+  }
+  MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
+
+  if (taps) {
+    if (taps->block_m) *taps->block_m = p.block_m;
+    if (mx) {
+      if (taps->xq) MOE_TRY(hipMemcpyAsync(taps->xq, xq, (size_t)T * H / 2, hipMemcpyDeviceToDevice, s));
+      if (taps->xs) MOE_TRY(hipMemcpyAsync(taps->xs, xs, (size_t)T * H / 32, hipMemcpyDeviceToDevice, s));
+      if (taps->aq) MOE_TRY(moe_k_gather_rows(aq, I / 2, pos, P, taps->aq, s));
+      if (taps->as) MOE_TRY(moe_k_gather_rows(as, I / 32, pos, P, taps->as, s));
+    } else {
+      if (taps->xq || taps->xs) {
+        if (!taps->xq || !taps->xs) return MOE_ERR_INVALID_ARG;
+        MOE_TRY(moe_k_fp8pair_to_int8(xq, (const float*)xs, H, nullptr, T, (int8_t*)taps->xq, (float*)taps->xs, s));
+      }
+      if (taps->aq || taps->as) {
+        if (!taps->aq || !taps->as) return MOE_ERR_INVALID_ARG;
+        MOE_TRY(moe_k_fp8pair_to_int8(aq, (const float*)as, I, pos, P, (int8_t*)taps->aq, (float*)taps->as, s));
+      }
+    }
+    if (taps->y) MOE_TRY(hipMemcpyAsync(taps->y, y, (size_t)P * H * 4, hipMemcpyDeviceToDevice, s));
+    if (taps->counts) MOE_TRY(hipMemcpyAsync(taps->counts, counts, (size_t)E * 4, hipMemcpyDeviceToDevice, s));
+    if (taps->offsets)
+      MOE_TRY(hipMemcpyAsync(taps->offsets, offsets, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice, s));
+    if (taps->sorted_pairs)
+      MOE_TRY(hipMemcpyAsync(taps->sorted_pairs, sorted, (size_t)p.cap * 4, hipMemcpyDeviceToDevice, s));
+    if (taps->pair_pos) MOE_TRY(hipMemcpyAsync(taps->pair_pos, pos, (size_t)P * 4, hipMemcpyDeviceToDevice, s));
+  }
+  return MOE_OK;
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
+                int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_forward_taps(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+int moe_rmsnorm(int32_t T, int32_t H, const float* x, float* out, void* stream) {
+  if (T < 0 || H < 64 || H % 64 || H > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_INVALID_ARG;
+  if (overlaps(x, (size_t)T * H * 4, out, (size_t)T * H * 4)) return MOE_ERR_ALIAS;
+  MOE_TRY(moe_k_rmsnorm(x, T, H, out, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_residual_add(int64_t n, float* x, const float* y, void* stream) {
+  if (n < 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!x || !y) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(moe_k_residual(x, y, n, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

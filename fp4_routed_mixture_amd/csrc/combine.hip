@@ -1,0 +1,74 @@
+// Weighted combine of the routed experts' outputs, and the two helpers of the
+// stacked-layer residual stream.
+//   combine : out[t][n] = fma chain over slots j = 0..k-1 of w[t][j] * y[t*k+j][n],
+//             starting from 0 (y rows are indexed by pair, so a token's k rows
+//             are adjacent).
+//   rmsnorm : out = x / sqrt(ss / H + 1e-6), ss in the router's fixed order
+//             (64 chunk chains, pairwise tree), one wave per row.
+//   residual: x += y.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w, int T,
+                                                      int H, int K, float* __restrict__ out) {
+  const size_t n4 = (size_t)T * (H >> 2);
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / (H >> 2);
+    const int n = (int)(i - t * (H >> 2)) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < K; ++j) {
+      const float wj = w[t * K + j];
+      const float4 v = *reinterpret_cast<const float4*>(y + (t * K + j) * (size_t)H + n);
+      acc.x = __builtin_fmaf(wj, v.x, acc.x);
+      acc.y = __builtin_fmaf(wj, v.y, acc.y);
+      acc.z = __builtin_fmaf(wj, v.z, acc.z);
+      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(out + t * H + n) = acc;
+  }
+}
+
+__global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ x, int H, float* __restrict__ out) {
+  const int t = blockIdx.x, c = threadIdx.x;
+  const int L = H >> 6;
+  const float* row = x + (size_t)t * H;
+  const float* chunk = row + (size_t)c * L;
+  float p = 0.0f;
+  for (int i = 0; i < L; ++i) p = __builtin_fmaf(chunk[i], chunk[i], p);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) p = p + __shfl_xor(p, o, 64);
+  const float r = __builtin_sqrtf(p / (float)H + 1e-6f);
+  for (int i = c; i < H; i += 64) out[(size_t)t * H + i] = row[i] / r;
+}
+
+__global__ __launch_bounds__(256) void residual_kernel(float* __restrict__ x, const float* __restrict__ y, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    x[i] = x[i] + y[i];
+}
+
+int grid_for(size_t n) {
+  size_t b = (n + 255) / 256;
+  return (int)(b < 65536 ? (b ? b : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t moe_k_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  combine_kernel<<<grid_for((size_t)T * (H >> 2)), 256, 0, st>>>(y, w, T, H, K, out);
+  return hipGetLastError();
+}
+
+hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  rmsnorm_kernel<<<T, 64, 0, st>>>(x, H, out);
+  return hipGetLastError();
+}
+
+hipError_t moe_k_residual(float* x, const float* y, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  residual_kernel<<<grid_for((size_t)n), 256, 0, st>>>(x, y, n);
+  return hipGetLastError();
+}

@@ -1,0 +1,55 @@
+// Internal launchers (host side). Every launcher enqueues on `st` and returns
+// the launch status; argument checking happens in the C-ABI layer (api.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// prepack.hip
+size_t moe_k_packed_scale_bytes(int which, int E, int N, int K);
+hipError_t moe_k_pack(int which, int E, int N, int K, const uint8_t* codes, const uint8_t* scales,
+                      const int32_t* perm, uint8_t* pcodes, uint8_t* pscales, hipStream_t st);
+hipError_t moe_k_unpack(int which, int E, int N, int K, const uint8_t* pcodes, const uint8_t* pscales,
+                        uint8_t* codes, uint8_t* scales, hipStream_t st);
+
+// route.hip
+hipError_t moe_k_router_logits(int x_dtype, const void* x, const float* wr, const float* bias, float* logits,
+                               int T, int H, int E, hipStream_t st);
+hipError_t moe_k_router_logits_variant(int variant, int x_dtype, const void* x, const float* wr, const float* bias,
+                                       float* logits, int T, int H, int E, hipStream_t st);
+hipError_t moe_k_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t st);
+
+// sort.hip
+size_t moe_k_sort_scratch_bytes(int P, int E);
+hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
+                      int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
+                      hipStream_t st);
+
+// quant.hip
+hipError_t moe_k_quant_int8(int in_dtype, const void* v, int rows, int K, int out_fp8pair, void* q, float* scales,
+                            const int32_t* sorted, int P, const int32_t* n_rows, hipStream_t st);
+hipError_t moe_k_quant_mxfp4(int in_dtype, const void* v, int rows, int K, uint8_t* codes, uint8_t* scales,
+                             hipStream_t st);
+hipError_t moe_k_fp8pair_to_int8(const uint8_t* src, const float* src_s, int K, const int32_t* row_of, int nrows,
+                                 int8_t* q, float* s, hipStream_t st);
+hipError_t moe_k_gather_rows(const void* src, int row_bytes, const int32_t* row_of, int nrows, void* dst,
+                             hipStream_t st);
+
+// gemm_decode.hip
+hipError_t moe_k_decode_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act8,
+                             const float* act_s, const int32_t* sorted, const int32_t* tile_expert,
+                             const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
+                             int rows_are_tokens, float* out, int out_ld, hipStream_t st);
+
+// gemm_prefill.hip
+int moe_k_prefill_block_m();
+int moe_k_prefill_jb();
+hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
+                              const uint8_t* act_scales, const int32_t* sorted, const int32_t* tile_expert,
+                              const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
+                              int rows_are_tokens, uint8_t* aq, uint8_t* as, float* y, int out_n, hipStream_t st);
+
+// combine.hip
+hipError_t moe_k_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st);
+hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t st);
+hipError_t moe_k_residual(float* x, const float* y, int64_t n, hipStream_t st);

@@ -1,0 +1,56 @@
+// Device side of the seeded input generator (not part of the layer): fills
+// packed E2M1 code bytes and E8M0 scale bytes with the SplitMix64 counter
+// stream described in synth.py (Steele, Lea and Flood 2014): output i of the
+// stream with key K is mix(K + (i + 1) * 0x9E3779B97F4A7C15), each output
+// gives eight little-endian bytes; a scale byte is 121 + (byte mod 5).
+// Used to place the 43-layer stack (about 147 GB) in HBM without a host copy.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ void fill_kernel(uint64_t key, uint64_t first_word, uint64_t nwords, int scale_mode, uint64_t* __restrict__ out) {
+  for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < nwords; i += (uint64_t)gridDim.x * blockDim.x) {
+    uint64_t v = mix64(key + (first_word + i + 1) * 0x9E3779B97F4A7C15ull);
+    if (scale_mode) {
+      uint64_t r = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) r |= (uint64_t)(121 + ((v >> (8 * b)) & 0xFF) % 5) << (8 * b);
+      v = r;
+    }
+    out[i] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t synth_stream_key(int seed, int layer, int tensor) {
+  uint64_t z = ((uint64_t)seed << 40) | ((uint64_t)layer << 16) | (uint64_t)tensor;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Fill nbytes (multiple of 8) at dst with bytes [first_byte, first_byte + nbytes)
+// of the (seed, layer, tensor) stream; scale_mode != 0 maps bytes to 121..125.
+int synth_fill(int seed, int layer, int tensor, uint64_t first_byte, uint64_t nbytes, int scale_mode, void* dst,
+               void* stream) {
+  if ((first_byte & 7) || (nbytes & 7) || !dst || ((uintptr_t)dst & 7)) return 1;
+  uint64_t nwords = nbytes / 8;
+  if (!nwords) return 0;
+  uint64_t blocks = (nwords + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  fill_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(synth_stream_key(seed, layer, tensor), first_byte / 8,
+                                                                 nwords, scale_mode, (uint64_t*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+/*
+ * fp4moe.h -- C ABI of the routed mixture-of-experts layer with packed FP4
+ * experts, written for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The layer is the "FP4 routed mixture-of-experts computation" of the
+ * DeepSeek-V4-Flash paper ("DeepSeek-V4-Flash on AMD gfx90a: Correctness
+ * Recovery and Inference Performance Engineering", abstract): packed FP4
+ * expert weights, INT8 activation quantization for decode, expert sorting,
+ * and a load-time repair of the weight layout. The model facts (256 routed
+ * experts, 6 active per token) are those of "DeepSeek V4 Flash on 8x AMD
+ * gfx1201: packaged TP=8 deployment", section "What we set out to do".
+ *
+ * For one batch of T tokens it computes
+ *   l[t,e]   = <x[t,:], Wr[e,:]> (+ b[e])               fp32, fixed order
+ *   s        = sigmoid(l); the top_k largest per token, ties to the lower
+ *              expert; w_j = s_j / sum_j s_j
+ *   sort     : stable counting sort of the P = T*top_k (token, slot) pairs
+ *   xq       = quant(x)      int8 per token, or MXFP4 (E2M1 + E8M0 per 32)
+ *   h        = xq @ W13[e]^T with E2M1 weights, one E8M0 scale per 32 along K
+ *   a        = silu(h[:I]) * h[I:],  aq = quant(a)
+ *   y        = aq @ W2[e]^T
+ *   out[t]   = sum_j w_j * y[t, j]
+ *
+ * Numerics (identical on every call and every run):
+ *   - Router dot products: H is split into 64 contiguous chunks; each chunk is
+ *     an fp32 fused-multiply-add chain over ascending k from 0; the 64 chunk
+ *     sums are added as a perfect pairwise tree in index order; then the bias
+ *     is added. sigmoid(z) = 1 / (1 + exp(-z)) with an exp built only from
+ *     IEEE fp32 operations (Cody-Waite reduction by ln 2, degree-7 Taylor
+ *     polynomial, exact power-of-two scaling).
+ *   - int8 quantization of a row: s = amax / 127, q = clamp(rint(v / s), +-127).
+ *   - MXFP4 quantization of 32 values (OCP Microscaling v1.0): scale exponent
+ *     floor(log2 amax) - 2 biased by 127; values scaled by an exact power of
+ *     two, rounded to nearest-even on the E2M1 grid, saturated at 6; the
+ *     code's sign is the value's sign bit.
+ *   - GEMM blocks of 32 along K are exact integer sums of code products; the
+ *     scaled block sums are accumulated in fp32; an int8 row scale multiplies
+ *     the finished sum.
+ *   - a = (g * sigmoid(g)) * u; out = fma chain over slots j = 0..top_k-1.
+ *
+ * Conventions for every call below:
+ *   - Array arguments are DEVICE pointers owned by the caller. The library
+ *     never allocates or frees device memory in these calls and keeps no
+ *     pointer after returning. Scratch memory comes from the caller's
+ *     workspace, whose contents are undefined afterwards.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *     enqueue work; they never synchronize the stream. Results are ready when
+ *     the stream's work has completed.
+ *   - Arguments are checked on the host before anything is launched; on any
+ *     error nothing is launched and the status says why. Launch failures
+ *     return MOE_ERR_HIP with the HIP error code kept per thread
+ *     (moe_last_hip_error). Faults inside kernels surface at the caller's
+ *     next synchronization. No exception or abort crosses this interface.
+ *   - Outputs are fully overwritten and bit-identical from run to run (no
+ *     floating-point atomics anywhere).
+ *   - Calls may run concurrently on different streams if they use different
+ *     workspaces and outputs.
+ *   - Shape limits: 1 <= T <= 1<<20, H % 256 == 0, 256 <= H <= 16384,
+ *     I % 128 == 0, 128 <= I <= 16384, 1 <= E <= 1024, 1 <= top_k <= min(E, 16).
+ *     T = 0 is accepted and does nothing.
+ *   - Alignment: weights, x, out, quantized buffers: 16 bytes.
+ */
+#ifndef FP4MOE_H
+#define FP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4MOE_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,         /* NULL where a pointer is required, bad enum value */
+    MOE_ERR_UNSUPPORTED_SHAPE = 2,   /* outside the shape limits above */
+    MOE_ERR_ALIGNMENT = 3,           /* a pointer is not 16-byte aligned */
+    MOE_ERR_ALIAS = 4,               /* an output overlaps an input */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < moe_workspace_size() */
+    MOE_ERR_HIP = 6                  /* a HIP call failed; see moe_last_hip_error() */
+};
+
+enum moe_x_dtype { MOE_X_F32 = 0, MOE_X_BF16 = 1 };       /* activation element type */
+enum moe_act_mode { MOE_ACT_INT8 = 0, MOE_ACT_MXFP4 = 1 }; /* activation quantization */
+enum moe_weight { MOE_W13 = 0, MOE_W2 = 1 };               /* which expert matrix */
+
+/* Layer shape and modes. act_mode selects the quantization of x and of the
+ * intermediate activation (it changes the numbers, so it is never chosen
+ * automatically): MOE_ACT_INT8 runs the low-M decode kernels, MOE_ACT_MXFP4
+ * the scaled-FP4 MFMA grouped GEMM. */
+typedef struct moe_config {
+    int32_t T;        /* tokens in the batch */
+    int32_t H;        /* hidden size */
+    int32_t I;        /* expert intermediate size */
+    int32_t E;        /* routed experts */
+    int32_t top_k;    /* experts per token */
+    int32_t x_dtype;  /* enum moe_x_dtype */
+    int32_t act_mode; /* enum moe_act_mode */
+} moe_config;
+
+/* Optional copies of intermediate results of moe_forward_taps (any pointer
+ * may be NULL). Pair p = t * top_k + j.
+ *   xq, xs : quantized x. INT8: int8 [T][H] and fp32 [T]. MXFP4: codes
+ *            [T][H/2] (low nibble = even k) and E8M0 bytes [T][H/32].
+ *   aq, as : quantized activation per pair, like xq/xs with K = I, P rows.
+ *   y      : fp32 [P][H], the down projection of each pair before weighting.
+ *   counts, offsets, sorted_pairs, pair_pos : the expert sort used, as
+ *            moe_sort returns them for the block size the kernels used
+ *            (offsets [E+1]; sorted_pairs [offsets[E]]; pair_pos [P]).
+ *   block_m: receives that block size (host int32, may be NULL). */
+typedef struct moe_taps {
+    void* xq;
+    void* xs;
+    void* aq;
+    void* as;
+    float* y;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted_pairs;
+    int32_t* pair_pos;
+    int32_t* block_m;
+} moe_taps;
+
+/* FP4MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/* The hipError_t of this thread's last MOE_ERR_HIP (0 if none). */
+int moe_last_hip_error(void);
+
+/* Bytes of device workspace moe_forward / moe_forward_taps / moe_sort need
+ * for this configuration (256-byte aligned base required). */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* ---------------------------------------------------------------- weights --
+ * Expert weights are packed E2M1 codes with one E8M0 scale per 32 elements
+ * along K ("packed FP4 weights", abstract of the gfx90a paper; element and
+ * scale formats from OCP Microscaling v1.0).
+ * Canonical layout (the interchange format):
+ *   W13 (which = MOE_W13, N = 2I rows, K = H): codes [E][2I][H/2], scales
+ *       [E][2I][H/32]; rows 0..I-1 are the gate projection, I..2I-1 the up
+ *       projection.
+ *   W2  (which = MOE_W2, N = H rows, K = I): codes [E][H][I/2], scales
+ *       [E][H][I/32].
+ *   In a code byte the low nibble is the even element along K.
+ * moe_forward reads the PREPACKED layout that moe_prepack writes: tiles of
+ * 32 rows x 64 K in the operand order of the gfx950 32x32x64 scaled MFMA,
+ * gate and up tiles interleaved, scales grouped four K-tiles to a dword. The
+ * packing is a bijection; moe_unpack inverts it.
+ *
+ * "Repair the weight layout at load time" (abstract of the gfx90a paper):
+ * row_perm (device int32 [N], or NULL for the identity) makes packed row r
+ * hold canonical row row_perm[r] of every expert, codes and scales together.
+ * A matrix whose rows were stored in the permuted order pi is repaired by
+ * passing the inverse permutation. */
+int moe_prepacked_size(int32_t which, int32_t E, int32_t N, int32_t K,
+                       size_t* code_bytes, size_t* scale_bytes);
+int moe_prepack(int32_t which, int32_t E, int32_t N, int32_t K,
+                const uint8_t* codes, const uint8_t* scales, const int32_t* row_perm,
+                uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
+int moe_unpack(int32_t which, int32_t E, int32_t N, int32_t K,
+               const uint8_t* packed_codes, const uint8_t* packed_scales,
+               uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------- router --
+ * Sigmoid-score top-k routing. x: [T][H] fp32 or bf16 (cfg->x_dtype),
+ * router_w: fp32 [E][H], router_bias: fp32 [E] or NULL (added to the logit
+ * before the sigmoid, so it moves selection and weights).
+ * Outputs: topk_ids int32 [T][top_k] in selection order (highest score
+ * first), topk_w fp32 [T][top_k] renormalized weights:
+ * S = ((s_0 + s_1) + s_2) + ..., w_j = s_j / S (1/top_k if S == 0). */
+int moe_route(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+              int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ sort --
+ * "Retuned expert sorting" (abstract of the gfx90a paper): group the P pairs
+ * (p = t * top_k + j) by expert, keeping ascending p within an expert, each
+ * expert's segment padded up to a multiple of block_m (1 <= block_m <= 1024).
+ *   counts [E]          pairs per expert
+ *   offsets [E+1]       padded segment starts; offsets[E] = padded total
+ *   sorted_pairs [cap]  pair index at each padded position, P in padding;
+ *                       cap = P + min(E, P) * (block_m - 1)
+ *   pair_pos [P]        padded position of each pair
+ *   tile_expert [cap / block_m + 1]  expert of each block_m tile, in order
+ *   n_tiles [1]         offsets[E] / block_m  (stays on the device)
+ * Bit-exact: integers only. */
+int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids,
+             int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+             int32_t* tile_expert, int32_t* n_tiles,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------- quantize --
+ * Quantize rows of an activation matrix v [rows][K] (in_dtype: MOE_X_F32 or
+ * MOE_X_BF16) with cfg->act_mode ("INT8 activation quantization", abstract of
+ * the gfx90a paper; MXFP4 per OCP Microscaling v1.0).
+ *   INT8 : q int8 [rows][K], scales fp32 [rows]. K % 64 == 0.
+ *   MXFP4: q codes [rows][K/2], scales E8M0 [rows][K/32]. K % 64 == 0. */
+int moe_quantize(const moe_config* cfg, int32_t rows, int32_t K, int32_t in_dtype,
+                 const void* v, void* q, void* scales, void* stream);
+
+/* --------------------------------------------------------------- forward --
+ * The whole routed-MoE layer: route, sort, quantize x, gate/up GEMM with
+ * fused SiLU*mul and requantization, down GEMM, weighted combine.
+ *   x [T][H] (cfg->x_dtype), router_w fp32 [E][H], router_bias fp32 [E] or
+ *   NULL, w13/w13_scale and w2/w2_scale in the prepacked layout,
+ *   out fp32 [T][H] (overwritten; must not overlap x),
+ *   topk_ids_out int32 [T][top_k] and topk_w_out fp32 [T][top_k] or NULL,
+ *   workspace of at least moe_workspace_size(cfg) bytes, 256-byte aligned. */
+int moe_forward(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                float* out, int32_t* topk_ids_out, float* topk_w_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward that also copies the intermediates named in taps (NULL taps =
+ * moe_forward). The copies are extra kernels after the layer. */
+int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                     const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                     float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------- stacked-layer helpers --
+ * Residual stream between stacked MoE layers, x_{l+1} = x_l + moe_l(rmsnorm(x_l)):
+ * moe_rmsnorm: out[t] = x[t] / sqrt(ss / H + 1e-6), ss = the router's fixed-
+ *   order dot product of x[t] with itself; IEEE sqrt and division; unit gain.
+ *   x, out fp32 [T][H], H % 64 == 0; may not overlap.
+ * moe_residual_add: x[i] += y[i] for i < n (fp32). */
+int moe_rmsnorm(int32_t T, int32_t H, const float* x, float* out, void* stream);
+int moe_residual_add(int64_t n, float* x, const float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4MOE_H */

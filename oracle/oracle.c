@@ -316,9 +316,16 @@ void or_quant_mxfp4(int R, int K, const float* v, uint8_t* codes, uint8_t* scale
  *   isum_b = sum (2 cx_i)(2 cw_i);  acc = acc + isum_b * 2^(ex_b + ew_b - 256)
  *   out_n  = acc
  * (Each product isum_b * 2^m is exact; only the fp32 additions round.) */
+static void twice_table(int t[16])
+{
+    for (int c = 0; c < 16; ++c) t[c] = twice_e2m1(c);
+}
+
 static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t* wc,
                           const uint8_t* ws, float* out)
 {
+    int t2[16];
+    twice_table(t2);
     for (int n = 0; n < N; ++n) {
         const uint8_t* row = wc + (size_t)n * (K / 2);
         float acc = 0.0f;
@@ -326,7 +333,7 @@ static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t*
             int32_t isum = 0;
             for (int i = 0; i < 32; ++i) {
                 int k = 32 * b + i;
-                isum += (int32_t)q[k] * twice_e2m1(nibble(row, k));
+                isum += (int32_t)q[k] * t2[nibble(row, k)];
             }
             acc = acc + ldexpf((float)isum, (int)ws[(size_t)n * (K / 32) + b] - 128);
         }
@@ -337,6 +344,8 @@ static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t*
 static void gemm_row_mxfp4(int K, int N, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc,
                            const uint8_t* ws, float* out)
 {
+    int t2[16];
+    twice_table(t2);
     for (int n = 0; n < N; ++n) {
         const uint8_t* row = wc + (size_t)n * (K / 2);
         float acc = 0.0f;
@@ -344,7 +353,7 @@ static void gemm_row_mxfp4(int K, int N, const uint8_t* xc, const uint8_t* xs, c
             int32_t isum = 0;
             for (int i = 0; i < 32; ++i) {
                 int k = 32 * b + i;
-                isum += twice_e2m1(nibble(xc, k)) * twice_e2m1(nibble(row, k));
+                isum += t2[nibble(xc, k)] * t2[nibble(row, k)];
             }
             int sh = (int)xs[b] + (int)ws[(size_t)n * (K / 32) + b] - 256;
             acc = acc + ldexpf((float)isum, sh);

@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU parity tests: device setup through the C-ABI
+binding, oracle inputs from the host generators (never from the device)."""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_routed_mixture_amd import binding as B
+from fp4_routed_mixture_amd import synth as S
+from fp4_routed_mixture_amd import synth_device as SD
+
+TOL = 2e-3  # max |err| <= TOL * RMS(oracle output)
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    B.lib()  # fails loudly if the library is missing
+
+
+def sha(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def host_x(w: S.Workload, layer=0, T=None) -> np.ndarray:
+    return S.activations(w, layer, T)
+
+
+def oracle_experts(w: S.Workload, ids: np.ndarray, layer: int = 0):
+    """Per-expert canonical weights from the host generator for the experts
+    that appear in ids (None elsewhere)."""
+    need = set(np.unique(ids).tolist())
+    return [S.expert_weights(w, layer, e) if e in need else None for e in range(w.E)]
+
+
+def oracle_layer(w: S.Workload, x_rows: np.ndarray, layer: int = 0, intermediates=False, wr=None, bias="default"):
+    wr = S.router_weights(w, layer) if wr is None else wr
+    b = S.router_bias(w, layer) if isinstance(bias, str) else bias
+    ids, _ = oracle.route(x_rows, wr, b, w.top_k)
+    ex = oracle_experts(w, ids, layer)
+    return oracle.moe_layer(x_rows, wr, b, ex, w.top_k, w.act_mode, intermediates=intermediates)
+
+
+def run_forward(w: S.Workload, dev_layer: dict, x: torch.Tensor, taps: bool = False, T=None):
+    T = x.shape[0] if T is None else T
+    cfg = SD.config(w, T)
+    ws = SD.workspace(cfg)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    res = {"out": out, "ids": ids, "w": wts}
+    if taps:
+        P = T * w.top_k
+        mx = w.act_mode == S.ACT_MXFP4
+        H, I = w.H, w.I
+        t = {
+            "xq": torch.empty((T, H // 2) if mx else (T, H), dtype=torch.uint8 if mx else torch.int8, device="cuda"),
+            "xs": torch.empty((T, H // 32) if mx else (T,), dtype=torch.uint8 if mx else torch.float32, device="cuda"),
+            "aq": torch.empty((P, I // 2) if mx else (P, I), dtype=torch.uint8 if mx else torch.int8, device="cuda"),
+            "as": torch.empty((P, I // 32) if mx else (P,), dtype=torch.uint8 if mx else torch.float32, device="cuda"),
+            "y": torch.empty((P, H), dtype=torch.float32, device="cuda"),
+            "counts": torch.empty(w.E, dtype=torch.int32, device="cuda"),
+            "offsets": torch.empty(w.E + 1, dtype=torch.int32, device="cuda"),
+            "pair_pos": torch.empty(max(P, 1), dtype=torch.int32, device="cuda"),
+        }
+        bm_guess = 128 if mx else 16
+        t["sorted_pairs"] = torch.empty(P + min(w.E, P) * (bm_guess - 1) + 1, dtype=torch.int32, device="cuda")
+        bm = B.moe_forward_taps(cfg, x, dev_layer["router_w"], dev_layer["bias"], dev_layer["w13"], dev_layer["w13s"],
+                                dev_layer["w2"], dev_layer["w2s"], out, ids, wts, t, ws)
+        res.update(t)
+        res["block_m"] = bm
+    else:
+        B.moe_forward(cfg, x, dev_layer["router_w"], dev_layer["bias"], dev_layer["w13"], dev_layer["w13s"],
+                      dev_layer["w2"], dev_layer["w2s"], out, ids, wts, ws)
+    torch.cuda.synchronize()
+    return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in res.items()}
+
+
+def assert_close_rms(got: np.ndarray, ref: np.ndarray, tol: float = TOL, what: str = "out"):
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    err = float(np.max(np.abs(got.astype(np.float64) - ref.astype(np.float64))))
+    assert err <= tol * rms, f"{what}: max|err| {err:.4g} > {tol} * RMS {rms:.4g}"
+    return err, rms

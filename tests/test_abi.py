@@ -1,0 +1,118 @@
+"""The C-ABI library loads and exports every declared entry point; argument
+checking happens on the host before any launch (no GPU needed for these)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from fp4_routed_mixture_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from fp4_routed_mixture_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_version_and_status_strings(L):
+    assert B.moe_abi_version() == 1
+    for s in range(7):
+        assert B.moe_status_string(s) and B.moe_status_string(s) != "unknown status"
+    assert B.moe_status_string(99) == "unknown status"
+    assert B.moe_last_hip_error() == 0
+
+
+def cfg(**kw):
+    base = dict(T=4, H=4096, I=2048, E=256, top_k=6, x_dtype=1, act_mode=0)
+    base.update(kw)
+    return B.moe_config(*(base[n] for n in ("T", "H", "I", "E", "top_k", "x_dtype", "act_mode")))
+
+
+def ws_status(c):
+    n = C.c_size_t(0)
+    return B.lib().moe_workspace_size(C.byref(c), C.byref(n)), n.value
+
+
+def test_workspace_size_and_shape_checks(L):
+    st, n = ws_status(cfg())
+    assert st == 0 and n > 4 * 4096 * 2
+    st1, n1 = ws_status(cfg(act_mode=1, T=4604))
+    assert st1 == 0 and n1 > 4604 * 6 * 4096 * 4  # holds y
+    assert ws_status(cfg(H=300))[0] == 2
+    assert ws_status(cfg(I=96))[0] == 2
+    assert ws_status(cfg(E=2000))[0] == 2
+    assert ws_status(cfg(top_k=0))[0] == 2
+    assert ws_status(cfg(top_k=17))[0] == 2
+    assert ws_status(cfg(E=4, top_k=5))[0] == 2
+    assert ws_status(cfg(x_dtype=3))[0] == 1
+    assert ws_status(cfg(act_mode=2))[0] == 1
+    assert L.moe_workspace_size(None, None) == 1
+
+
+def test_prepacked_sizes(L):
+    cb, sb = B.moe_prepacked_size(0, 256, 4096, 4096)
+    assert cb == 256 * 4096 * 2048 and sb == 256 * 4096 * 128
+    cb, sb = B.moe_prepacked_size(1, 8, 256, 128)
+    # K=128: two K-tiles padded to four, one dword per (row, half) -> 8 bytes a row
+    assert cb == 8 * 256 * 64 and sb == 8 * 256 * 8
+    with pytest.raises(B.MoEError):
+        B.moe_prepacked_size(2, 8, 256, 128)
+    with pytest.raises(B.MoEError):
+        B.moe_prepacked_size(0, 8, 96, 256)
+
+
+FAKE = 0x10000  # never dereferenced: checks return before any launch
+
+
+def fwd(c, x=FAKE, wr=FAKE, w13=FAKE, out=FAKE + (1 << 30), ws=FAKE + (1 << 34), ws_bytes=1 << 40):
+    return B.lib().moe_forward(C.byref(c), x, wr, None, w13, FAKE, FAKE, FAKE, out, None, None, ws, ws_bytes, None)
+
+
+def test_forward_argument_errors(L):
+    c = cfg()
+    assert fwd(c, x=None) == 1
+    assert fwd(c, w13=None) == 1
+    assert fwd(c, out=None) == 1
+    assert fwd(c, ws=None) == 1
+    assert fwd(c, x=FAKE + 8) == 3              # misaligned x
+    assert fwd(c, ws=FAKE + (1 << 34) + 16) == 3  # workspace not 256-aligned
+    assert fwd(c, out=FAKE) == 4                 # out overlaps x
+    assert fwd(c, ws_bytes=100) == 5
+    assert fwd(cfg(H=100)) == 2
+    assert fwd(cfg(T=0), x=None, out=None) == 0  # empty batch: nothing to do
+
+
+def test_other_entry_point_errors(L):
+    c = cfg()
+    vp = C.c_void_p
+    assert L.moe_sort(C.byref(c), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert L.moe_sort(C.byref(c), 16, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.moe_quantize(C.byref(c), 4, 100, 0, FAKE, FAKE, FAKE, None) == 2
+    assert L.moe_quantize(C.byref(c), 4, 128, 5, FAKE, FAKE, FAKE, None) == 1
+    assert L.moe_quantize(C.byref(c), 4, 128, 0, FAKE + 4, FAKE, FAKE, None) == 3
+    assert L.moe_route(C.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.moe_route(C.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, None) == 5
+    assert L.moe_prepack(0, 8, 256, 256, FAKE, FAKE, None, FAKE, FAKE + (1 << 20), None) == 4  # codes overlap
+    assert L.moe_rmsnorm(2, 100, FAKE, FAKE + (1 << 20), None) == 2
+    assert L.moe_rmsnorm(2, 128, FAKE, FAKE + 4, None) == 4
+    assert L.moe_residual_add(-1, FAKE, FAKE, None) == 1
+    assert L.moe_residual_add(0, None, None, None) == 0
