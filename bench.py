@@ -1,0 +1,274 @@
+#!/usr/bin/env python
+"""Benchmark of the FP4 routed-MoE layer on one MI355X.
+
+A step is one moe_forward (route, sort, quantize, gate/up GEMM with SiLU*mul,
+down GEMM, combine) over one batch. The headline workload is the decode layer
+with 4 tokens (hidden 4096, intermediate 2048, 256 experts, top-6, bf16 x,
+int8 activations). Steps cycle through ROT distinct layers (weights and
+inputs drawn from different seeds' streams) so each step streams expert
+weights that the previous steps did not touch, as a 43-layer model's decode
+does; the 256 MB last-level cache cannot serve them.
+
+Prints one JSON line: tokens/s, the dominant kernel's roofline fraction
+(algorithmic bytes or FLOPs per launch / its average duration from HIP events
+recorded on the library's stream inside the timed region), and the CPU
+oracle's tokens/s on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA, published
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ----------------------------------------------------------------- HIP events
+class HipEvents:
+    def __init__(self):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            ev = C.c_void_p()
+            assert self.hip.hipEventCreate(C.byref(ev)) == 0
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = C.c_float()
+        assert self.hip.hipEventElapsedTime(C.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.hip.hipEventDestroy(ev)
+
+
+def per_expert_bytes(w):
+    H, I = w.H, w.I
+    w13 = 2 * I * H // 2 + 2 * I * H // 32
+    w2 = H * I // 2 + H * I // 32
+    return w13, w2
+
+
+def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, ev: HipEvents) -> dict:
+    w = S.WORKLOADS[name]
+    T = w.T
+    layers = [SD.load_layer(w, layer=l) for l in range(rot)]
+    xs = [SD.activations(w, layer=l) for l in range(rot)]
+    cfg = SD.config(w)
+    ws = SD.workspace(cfg)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    ids = [torch.empty((T, w.top_k), dtype=torch.int32, device="cuda") for _ in range(rot)]
+    wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    nst = len(B.STAGES)
+    events = [ev.create(2 * nst) for _ in range(steps)]
+
+    def step(i, evs=None):
+        r = i % rot
+        L = layers[r]
+        if evs is None:
+            B.moe_forward(cfg, xs[r], L["router_w"], L["bias"], L["w13"], L["w13s"], L["w2"], L["w2s"], out,
+                          ids[r], wts, ws)
+        else:
+            B.moe_forward_taps(cfg, xs[r], L["router_w"], L["bias"], L["w13"], L["w13s"], L["w2"], L["w2s"], out,
+                               ids[r], wts, {"events": evs}, ws)
+
+    for i in range(max(warmup, rot)):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {s: float(np.mean([ev.elapsed_ms(events[i][2 * k], events[i][2 * k + 1]) for i in range(steps)]))
+                for k, s in enumerate(B.STAGES)}
+    for e in events:
+        ev.destroy(e)
+
+    # routing statistics of each rotated batch (its distinct experts set the bytes)
+    distinct = []
+    max_load = []
+    for r in range(rot):
+        a = ids[r].cpu().numpy()
+        distinct.append(len(np.unique(a)))
+        max_load.append(int(np.bincount(a.ravel(), minlength=w.E).max()))
+    d_avg = float(np.mean([distinct[i % rot] for i in range(steps)]))
+    b13, b2 = per_expert_bytes(w)
+    xbytes = T * w.H * (2 if w.x_dtype == S.X_BF16 else 4)
+    P = T * w.top_k
+    layer_bytes = d_avg * (b13 + b2) + w.E * w.H * 4 + xbytes + T * w.H * 4
+    # gate/up kernel: weights of the routed experts + quantized x in + its output
+    if w.act_mode == S.ACT_INT8:
+        g1_bytes = d_avg * b13 + T * 2 * w.H + P * w.I * 4
+    else:
+        g1_bytes = d_avg * b13 + T * w.H // 2 + T * w.H // 32 + P * (w.I // 2 + w.I // 32)
+    g1_flops = 2.0 * P * w.H * 2 * w.I
+    layer_flops = 2.0 * P * (w.H * 2 * w.I + w.I * w.H)
+    ms_step = elapsed * 1e3 / steps
+    g1_ms = stage_ms["gate_up"]
+    return {
+        "workload": name, "T": T, "steps": steps, "rot": rot,
+        "ms_per_step": ms_step, "tokens_per_s": T / (ms_step / 1e3),
+        "stage_ms": stage_ms, "distinct_experts": d_avg, "max_load": max_load,
+        "layer_alg_bytes": layer_bytes, "layer_hbm_gbs": layer_bytes / (ms_step / 1e3) / 1e9,
+        "layer_fp4_tflops": layer_flops / (ms_step / 1e3) / 1e12,
+        "gate_up_alg_bytes": g1_bytes, "gate_up_ms": g1_ms,
+        "gate_up_gbs": g1_bytes / (g1_ms / 1e3) / 1e9,
+        "gate_up_tflops": g1_flops / (g1_ms / 1e3) / 1e12,
+    }
+
+
+def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
+    """The oracle, untuned, on the host cores: whole layers of the same
+    workload (rotating the same seeded batches) until about budget_s of CPU
+    work; for large batches a token sample (every output depends only on its
+    own token)."""
+    w = S.WORKLOADS[name]
+    T = min(w.T, 64)
+    batches = []
+    for l in range(4):
+        x = S.activations(w, l, T=w.T)[:T]
+        wr, b = S.router_weights(w, l), S.router_bias(w, l)
+        ids, _ = oracle.route(x, wr, b, w.top_k)
+        need = set(np.unique(ids).tolist())
+        ex = [S.expert_weights(w, l, e) if e in need else None for e in range(w.E)]
+        batches.append((x, wr, b, ex))
+    n_tok = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        x, wr, b, ex = batches[i % len(batches)]
+        oracle.moe_layer(x, wr, b, ex, w.top_k, w.act_mode)
+        n_tok += x.shape[0]
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": n_tok / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{i} whole-layer oracle calls of {name} ({T} tokens each, 4 seeded batches rotating), "
+                      f"{el:.1f} s wall, weight generation outside the timed region"}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the
+    kernel source is unchanged since they were taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    try:
+        rec = json.load(open(PROFILE_TRAFFIC))[f"{kernel}@{workload}"]
+    except (KeyError, ValueError):
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "fp4_routed_mixture_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_t4")
+    ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
+    ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is not sharded here",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no HIP device visible)", file=sys.stderr)
+        sys.exit(1)
+    from fp4_routed_mixture_amd import binding as B
+    from fp4_routed_mixture_amd import synth as S
+    from fp4_routed_mixture_amd import synth_device as SD
+    B.lib()
+    ev = HipEvents()
+
+    main_res = run_workload(args.workload, args.steps, args.warmup, args.rot, torch, B, S, SD, ev)
+    print(f"# {args.workload}: {main_res['ms_per_step'] * 1e3:.1f} us/step, {main_res['tokens_per_s']:.0f} tok/s, "
+          f"stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in main_res["stage_ms"].items()),
+          file=sys.stderr, flush=True)
+    legs = {}
+    if not args.no_legs:
+        for name, steps, rot in (("decode_t64_zipf", 30, 8), ("prefill_t4604_zipf", 10, 2)):
+            torch.cuda.empty_cache()
+            r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev)
+            legs[name] = r
+            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tokens_per_s']:.0f} tok/s, "
+                  f"layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
+                  + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
+
+    w = S.WORKLOADS[args.workload]
+    mx = w.act_mode == S.ACT_MXFP4
+    if mx:
+        ach, peak, unit, bound = main_res["gate_up_tflops"], FP4_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = main_res["gate_up_gbs"], HBM_PEAK_GBS, "GB/s", "hbm"
+    kernel = "prefill_gemm_kernel<true>" if mx else "decode_gemm_kernel<true>"
+    roof = {"bound": bound, "kernel": kernel, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic_for(kernel, args.workload),
+            "layer_hbm_gbs": round(main_res["layer_hbm_gbs"], 1),
+            "layer_hbm_frac": round(main_res["layer_hbm_gbs"] / HBM_PEAK_GBS, 4)}
+
+    import oracle
+    cpu = cpu_baseline(args.workload, args.cpu_seconds, S, oracle)
+
+    line = {
+        "metric": "routed-MoE tokens/s; decode HBM GB/s and prefill FP4 MFMA % of peak",
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if mx else "fp4xint8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.top_k,
+                   "x": "bf16" if w.x_dtype == S.X_BF16 else "fp32", "act": "mxfp4" if mx else "int8",
+                   "routing": "zipf1.1" if w.zipf else "uniform", "distinct_layers_cycled": args.rot},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stage_us": {k: round(v * 1e3, 2) for k, v in main_res["stage_ms"].items()},
+        "distinct_experts": main_res["distinct_experts"],
+        "legs": {k: {"tokens_per_s": round(v["tokens_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
+                     "layer_hbm_gbs": round(v["layer_hbm_gbs"], 1),
+                     "layer_hbm_frac": round(v["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
+                     "layer_fp4_tflops": round(v["layer_fp4_tflops"], 1),
+                     "layer_fp4_frac": round(v["layer_fp4_tflops"] / FP4_PEAK_TFLOPS, 4),
+                     "gate_up_gbs": round(v["gate_up_gbs"], 1), "gate_up_tflops": round(v["gate_up_tflops"], 1),
+                     "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
+                     "distinct_experts": v["distinct_experts"]} for k, v in legs.items()},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

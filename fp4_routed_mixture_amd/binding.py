@@ -20,6 +20,7 @@ MOE_OK = 0
 MOE_X_F32, MOE_X_BF16 = 0, 1
 MOE_ACT_INT8, MOE_ACT_MXFP4 = 0, 1
 MOE_W13, MOE_W2 = 0, 1
+STAGES = ["router", "topk", "quant_x", "sort", "gate_up", "requant", "down", "combine"]
 
 # every function that include/fp4moe.h declares
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_workspace_size",
@@ -46,7 +47,8 @@ class moe_config(C.Structure):
 class moe_taps(C.Structure):
     _fields_ = [("xq", C.c_void_p), ("xs", C.c_void_p), ("aq", C.c_void_p), ("as_", C.c_void_p),
                 ("y", C.c_void_p), ("counts", C.c_void_p), ("offsets", C.c_void_p),
-                ("sorted_pairs", C.c_void_p), ("pair_pos", C.c_void_p), ("block_m", C.c_void_p)]
+                ("sorted_pairs", C.c_void_p), ("pair_pos", C.c_void_p), ("block_m", C.c_void_p),
+                ("events", C.c_void_p)]
 
 
 _lib = None
@@ -177,11 +179,13 @@ def moe_forward(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out
 def moe_forward_taps(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
                      taps: dict, workspace, stream=None):
     """taps: dict with any of xq, xs, aq, as, y, counts, offsets, sorted_pairs,
-    pair_pos (device tensors). Returns the block size the kernels used."""
+    pair_pos (device tensors) and events (a ctypes array of 2*len(STAGES)
+    hipEvent_t handles). Returns the block size the kernels used."""
     bm = C.c_int32(0)
+    ev = taps.get("events")
     t = moe_taps(*(_p(taps.get(n)) for n in ("xq", "xs", "aq", "as", "y", "counts", "offsets",
                                               "sorted_pairs", "pair_pos")),
-                 C.cast(C.pointer(bm), C.c_void_p))
+                 C.cast(C.pointer(bm), C.c_void_p), None if ev is None else C.cast(ev, C.c_void_p))
     _check(lib().moe_forward_taps(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(w13), _p(w13_scale),
                                   _p(w2), _p(w2_scale), _p(out), _p(topk_ids_out), _p(topk_w_out), C.byref(t),
                                   _p(workspace), workspace.numel(), _s(stream)), "moe_forward_taps")

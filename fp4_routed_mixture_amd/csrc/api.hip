@@ -240,31 +240,57 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
   void* as = at<void>(workspace, p.as);
   float* y = at<float>(workspace, p.y);
   const int P = p.P;
+  void* const* ev = taps ? taps->events : nullptr;
+  auto mark = [&](int i) -> hipError_t {
+    return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+  };
 
   // route
+  MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
   MOE_TRY(moe_k_router_logits(cfg->x_dtype, x, router_w, router_bias, logits, T, H, E, s));
+  MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
+  MOE_TRY(mark(2 * MOE_STAGE_TOPK));
   MOE_TRY(moe_k_topk(logits, T, E, k, ids, w, s));
+  MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
   // quantize x
+  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));
   if (mx)
     MOE_TRY(moe_k_quant_mxfp4(cfg->x_dtype, x, T, H, xq, (uint8_t*)xs, s));
   else
     MOE_TRY(moe_k_quant_int8(cfg->x_dtype, x, T, H, 1, xq, (float*)xs, nullptr, 0, nullptr, s));
+  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
   // sort
+  MOE_TRY(mark(2 * MOE_STAGE_SORT));
   MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
+  MOE_TRY(mark(2 * MOE_STAGE_SORT + 1));
   // expert GEMMs
   if (mx) {
+    MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
     MOE_TRY(moe_k_prefill_gemm(1, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, ntiles, p.max_tiles, H,
                                I / 32, k, P, 1, aq, (uint8_t*)as, nullptr, I, s));
+    MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
+    MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_DOWN));
     MOE_TRY(moe_k_prefill_gemm(0, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
                                H / 32, k, P, 0, nullptr, nullptr, y, H, s));
+    MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
   } else {
+    MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
     MOE_TRY(moe_k_decode_gemm(1, w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I / 32,
                               k, P, 1, a, I, s));
+    MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
     MOE_TRY(moe_k_quant_int8(MOE_X_F32, a, p.cap, I, 1, aq, (float*)as, sorted, P, offsets + E, s));
+    MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_DOWN));
     MOE_TRY(moe_k_decode_gemm(0, w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, I, H / 32,
                               k, P, 0, y, H, s));
+    MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
   }
+  MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
   MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
+  MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
 
   if (taps) {
     if (taps->block_m) *taps->block_m = p.block_m;

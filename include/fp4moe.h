@@ -110,7 +110,23 @@ typedef struct moe_config {
  *   counts, offsets, sorted_pairs, pair_pos : the expert sort used, as
  *            moe_sort returns them for the block size the kernels used
  *            (offsets [E+1]; sorted_pairs [offsets[E]]; pair_pos [P]).
- *   block_m: receives that block size (host int32, may be NULL). */
+ *   block_m: receives that block size (host int32, may be NULL).
+ *   events : NULL, or 2 * MOE_N_STAGES hipEvent_t handles (host array); the
+ *            library records events[2*i] on the stream before stage i and
+ *            events[2*i+1] after it, so a caller can time each stage on the
+ *            stream the kernels run on. A stage that launches nothing for
+ *            this configuration records both events back to back. */
+enum moe_stage {
+    MOE_STAGE_ROUTER = 0,  /* router logits */
+    MOE_STAGE_TOPK = 1,    /* sigmoid, top-k, renormalization */
+    MOE_STAGE_QUANT_X = 2, /* activation quantization of x */
+    MOE_STAGE_SORT = 3,    /* expert sort */
+    MOE_STAGE_GATE_UP = 4, /* gate/up GEMM with SiLU*mul (and MXFP4 requant) */
+    MOE_STAGE_REQUANT = 5, /* int8 requantization of the activation */
+    MOE_STAGE_DOWN = 6,    /* down GEMM */
+    MOE_STAGE_COMBINE = 7, /* weighted combine */
+    MOE_N_STAGES = 8
+};
 typedef struct moe_taps {
     void* xq;
     void* xs;
@@ -122,6 +138,7 @@ typedef struct moe_taps {
     int32_t* sorted_pairs;
     int32_t* pair_pos;
     int32_t* block_m;
+    void* const* events;
 } moe_taps;
 
 /* FP4MOE_ABI_VERSION of the built library. */
@@ -216,8 +233,10 @@ int moe_forward(const moe_config* cfg, const void* x, const float* router_w, con
                 float* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* moe_forward that also copies the intermediates named in taps (NULL taps =
- * moe_forward). The copies are extra kernels after the layer. */
+/* moe_forward that also copies the intermediates named in taps and records
+ * the stage events (NULL taps = moe_forward). The copies are extra kernels
+ * after the layer. sorted_pairs needs P + min(E, P) * (block_m - 1) entries
+ * (block_m = 16 for MOE_ACT_INT8, 128 for MOE_ACT_MXFP4). */
 int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                      const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
                      float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps,
