@@ -43,15 +43,16 @@ int check_shape(const moe_config* c) {
 
 // Workspace plan of one layer call.
 struct Plan {
-  int block_m, P, cap, max_tiles;
-  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, a, aq, as, y, total;
+  int block_m, P, cap, max_tiles, n_counters;
+  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, counters, a, aq, as, y,
+      total;
 };
 
 Plan make_plan(const moe_config* c) {
   Plan p;
   const int T = c->T, H = c->H, I = c->I, E = c->E, k = c->top_k;
   const bool mx = c->act_mode == MOE_ACT_MXFP4;
-  p.block_m = mx ? moe_k_prefill_block_m() : 16;
+  p.block_m = mx ? moe_k_prefill_block_m() : moe_k_decode_block_m();
   p.P = T * k;
   p.cap = p.P + (E < p.P ? E : p.P) * (p.block_m - 1);
   p.max_tiles = p.cap / p.block_m;
@@ -61,7 +62,7 @@ Plan make_plan(const moe_config* c) {
     off += up256(bytes);
     return o;
   };
-  p.logits = take((size_t)T * E * 4);
+  p.logits = take(moe_k_router_partial_bytes(T, H, E));
   p.ids = take((size_t)p.P * 4);
   p.w = take((size_t)p.P * 4);
   p.xq = take(mx ? (size_t)T * H / 2 : (size_t)T * 2 * H);
@@ -73,6 +74,10 @@ Plan make_plan(const moe_config* c) {
   p.tiles = take((size_t)(p.max_tiles + 1) * 4);
   p.ntiles = take(4);
   p.sort_scratch = take(moe_k_sort_scratch_bytes(p.P, E));
+  // completion counters of the fused decode epilogues: one per sort tile
+  // (gate/up) and one per (token, 32-column block) (down)
+  p.n_counters = mx ? 0 : p.max_tiles + T * (H / 32);
+  p.counters = take((size_t)p.n_counters * 4);
   p.a = take(mx ? 0 : (size_t)p.cap * I * 4);
   p.aq = take(mx ? (size_t)p.cap * I / 2 : (size_t)p.cap * 2 * I);
   p.as = take(mx ? (size_t)p.cap * I / 32 : (size_t)p.cap * 4);
@@ -159,11 +164,13 @@ int moe_route(const moe_config* cfg, const void* x, const float* router_w, const
   if (!x || !router_w || !topk_ids || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
   Plan p = make_plan(cfg);
-  if (workspace_bytes < p.logits + (size_t)cfg->T * cfg->E * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < p.logits + moe_k_router_partial_bytes(cfg->T, cfg->H, cfg->E))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
-  float* logits = at<float>(workspace, p.logits);
-  MOE_TRY(moe_k_router_logits(cfg->x_dtype, x, router_w, router_bias, logits, cfg->T, cfg->H, cfg->E, s));
-  MOE_TRY(moe_k_topk(logits, cfg->T, cfg->E, cfg->top_k, topk_ids, topk_w, s));
+  float* partial = at<float>(workspace, p.logits);
+  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, s));
+  MOE_TRY(moe_k_topk_quant(cfg->x_dtype, partial, router_bias, x, cfg->T, cfg->H, cfg->E, cfg->top_k, 0, 0, topk_ids,
+                           topk_w, nullptr, nullptr, s));
   return MOE_OK;
 }
 
@@ -181,7 +188,7 @@ int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids, in
   if (scratch && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
   if (workspace_bytes < scratch) return MOE_ERR_WORKSPACE_TOO_SMALL;
   MOE_TRY(moe_k_sort(topk_ids, P, cfg->E, block_m, counts, offsets, sorted_pairs, pair_pos, tile_expert, n_tiles,
-                     workspace, (hipStream_t)stream));
+                     workspace, nullptr, 0, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -241,27 +248,24 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
   float* y = at<float>(workspace, p.y);
   const int P = p.P;
   void* const* ev = taps ? taps->events : nullptr;
-  auto mark = [&](int i) -> hipError_t {
-    return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
-  };
+  auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
 
-  // route
+  int32_t* counters = at<int32_t>(workspace, p.counters);
+  const int nt2 = H / 32;
+
+  // route (+ for P <= 1024: top-k, sort and quantization of x in one kernel)
   MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
-  MOE_TRY(moe_k_router_logits(cfg->x_dtype, x, router_w, router_bias, logits, T, H, E, s));
+  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, s));
   MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
   MOE_TRY(mark(2 * MOE_STAGE_TOPK));
-  MOE_TRY(moe_k_topk(logits, T, E, k, ids, w, s));
+  MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, 1, mx, ids, w, xq, (uint8_t*)xs, s));
   MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
-  // quantize x
-  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));
-  if (mx)
-    MOE_TRY(moe_k_quant_mxfp4(cfg->x_dtype, x, T, H, xq, (uint8_t*)xs, s));
-  else
-    MOE_TRY(moe_k_quant_int8(cfg->x_dtype, x, T, H, 1, xq, (float*)xs, nullptr, 0, nullptr, s));
+  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
   MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
-  // sort
+  // sort (also clears the fused epilogues' completion counters)
   MOE_TRY(mark(2 * MOE_STAGE_SORT));
-  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
+  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, counters,
+                     p.n_counters, s));
   MOE_TRY(mark(2 * MOE_STAGE_SORT + 1));
   // expert GEMMs
   if (mx) {
@@ -275,22 +279,26 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
     MOE_TRY(moe_k_prefill_gemm(0, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
                                H / 32, k, P, 0, nullptr, nullptr, y, H, s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
+    MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
+    MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   } else {
+    // gate/up with the int8 requantization fused (last workgroup of a tile)
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
-    MOE_TRY(moe_k_decode_gemm(1, w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I / 32,
-                              k, P, 1, a, I, s));
+    MOE_TRY(moe_k_decode_gate_up(w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I, k,
+                                 P, a, counters, aq, (float*)as, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
-    MOE_TRY(moe_k_quant_int8(MOE_X_F32, a, p.cap, I, 1, aq, (float*)as, sorted, P, offsets + E, s));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
+    // down with the combine fused (last arrival per token and column block)
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
-    MOE_TRY(moe_k_decode_gemm(0, w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, I, H / 32,
-                              k, P, 0, y, H, s));
+    MOE_TRY(moe_k_decode_down(w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, H, I, k, P, y,
+                              counters + p.max_tiles, w, out, s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
+    MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   }
-  MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
-  MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
-  MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
+  (void)nt2;
 
   if (taps) {
     if (taps->block_m) *taps->block_m = p.block_m;

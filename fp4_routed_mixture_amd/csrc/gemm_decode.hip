@@ -17,13 +17,25 @@
 // K into contiguous ranges of four-K-tile groups and reduce through LDS in a
 // fixed order. Weights stream straight from HBM into MFMA registers: the
 // prepacked layout makes each wave's load of a 32x64 tile one contiguous
-// 1 KB (16 B per lane).
-// Epilogue W13: a = (g * sigmoid(g)) * u in fp32 into a[pos][I].
-// Epilogue W2 : y[pair][H] = s_a * sum.
+// 1 KB (16 B per lane); the next group's loads are issued before the current
+// group's MFMAs.
+//
+// Fused epilogues (deterministic: every value is produced by one workgroup in
+// a fixed order; counters only decide WHICH workgroup does the final step):
+//   gate/up: a = (g * sigmoid(g)) * u in fp32 into a[pos][I]; the last of the
+//            I/32 workgroups of sort tile q (a per-tile counter) requantizes
+//            the tile's rows to int8 (s = amax/127) as FP8 hi/lo planes.
+//   down   : y[pair][H] = s_a * sum; the workgroup that completes column block
+//            j of a token (a per (token, j) counter reaching top_k) writes
+//            out[t][32j..32j+32) = fma chain over slots of w_j * y.
+// The workgroup that finishes resets its counter to 0, and the routing kernel
+// clears all counters at the start of every call.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
+
+constexpr int DM = 16;  // pair rows per sort tile
 
 template <int U>
 __device__ __forceinline__ v16f mfma_fp4_fp8(const v4i& a, const v8i& b, v16f acc, uint32_t sa, uint32_t sb) {
@@ -31,118 +43,286 @@ __device__ __forceinline__ v16f mfma_fp4_fp8(const v4i& a, const v8i& b, v16f ac
   return MFMA_FP4_FP8(a8, b, acc, U, (int)sa, 0, (int)sb);
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void decode_gemm_kernel(
-    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act8,
-    const float* __restrict__ act_s, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
-    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, int rows_are_tokens,
-    float* __restrict__ out, int out_ld) {
-  constexpr int S = GATE_UP ? 2 : 1;
-  __shared__ float red[4][S][16][64];
-  const int j = blockIdx.x, q = blockIdx.y;
-  if (q >= *n_tiles) return;
-  const int e = tile_expert[q];
+#ifndef DEC_NT
+#define DEC_NT 0       // non-temporal weight loads
+#endif
+#ifndef DEC_DB
+#define DEC_DB 0       // register double buffering of K-tile groups
+#endif
+#ifndef DEC_WAVES
+#define DEC_WAVES 4    // waves per workgroup (K split)
+#endif
+constexpr int NW = DEC_WAVES;
+
+template <int S>
+struct Group {
+  v4i a0[4], a1[4];
+  v8i b[4];
+  uint32_t sa0, sa1;
+};
+
+__device__ __forceinline__ v4i ld_weights(const uint8_t* p) {
+#if DEC_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+#else
+  return *reinterpret_cast<const v4i*>(p);
+#endif
+}
+
+template <int S>
+__device__ __forceinline__ void load_group(Group<S>& G, const uint8_t* aptr, const uint32_t* sptr, const uint8_t* bptr,
+                                           bool valid, int g, int KT) {
+  G.sa0 = sptr[(size_t)g * S * 64];
+  G.sa1 = S == 2 ? sptr[(size_t)g * S * 64 + 64] : 0u;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kt = g * 4 + u;
+    G.a0[u] = (v4i){0, 0, 0, 0};
+    G.a1[u] = (v4i){0, 0, 0, 0};
+    G.b[u] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    if (kt < KT) {
+      G.a0[u] = ld_weights(aptr + (size_t)kt * S * 1024);
+      if (S == 2) G.a1[u] = ld_weights(aptr + (size_t)kt * S * 1024 + 1024);
+      if (valid) {
+        const v4i lo = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64);
+        const v4i hi = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64 + 32);
+        G.b[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void mma_group(const Group<S>& G, v16f& acc0, v16f& acc1, uint32_t sb) {
+  // padded K-tiles (kt >= KT) carry zero operands: they add exactly 0
+  acc0 = mfma_fp4_fp8<0>(G.a0[0], G.b[0], acc0, G.sa0, sb);
+  acc0 = mfma_fp4_fp8<1>(G.a0[1], G.b[1], acc0, G.sa0, sb);
+  acc0 = mfma_fp4_fp8<2>(G.a0[2], G.b[2], acc0, G.sa0, sb);
+  acc0 = mfma_fp4_fp8<3>(G.a0[3], G.b[3], acc0, G.sa0, sb);
+  if (S == 2) {
+    acc1 = mfma_fp4_fp8<0>(G.a1[0], G.b[0], acc1, G.sa1, sb);
+    acc1 = mfma_fp4_fp8<1>(G.a1[1], G.b[1], acc1, G.sa1, sb);
+    acc1 = mfma_fp4_fp8<2>(G.a1[2], G.b[2], acc1, G.sa1, sb);
+    acc1 = mfma_fp4_fp8<3>(G.a1[3], G.b[3], acc1, G.sa1, sb);
+  }
+}
+
+// Main loop + cross-wave reduction. On return red[w][s][v][lane] holds every
+// wave's partial sums (read by the epilogue after __syncthreads()).
+template <int S>
+__device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+                                                const uint8_t* __restrict__ act8, int row, bool valid, int part, int e,
+                                                int j, int K, int NT, float (*red)[S][16][64]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KT = K >> 6, G = (KT + 3) >> 2;
-
-  // B operand
-  const int c = lane & 31, h = lane >> 5;
-  const int slot = c & 15, part = c >> 4;
-  const int p = q * 16 + slot;
-  const int pair = sorted[p];
-  const bool valid = pair < P;
-  const int row = rows_are_tokens ? (valid ? pair / top_k : 0) : p;
+  const int h = lane >> 5;
   const uint8_t* bptr = act8 + ((size_t)row * 2 + part) * K + h * 16;
   const uint32_t sb = part ? 0x7f7f7f7fu : 0x83838383u;  // lo: 2^0, hi: 2^4
-
-  // A operand
   const size_t tile = (size_t)e * NT + j;
   const uint8_t* aptr = wq + tile * KT * (S * 1024) + lane * 16;
   const uint32_t* sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (S * 256)) + lane;
-
-  const int g0 = (G * wave) >> 2, g1 = (G * (wave + 1)) >> 2;
+  const int g0 = (G * wave) / NW, g1 = (G * (wave + 1)) / NW;
   v16f acc0 = {}, acc1 = {};
-  for (int g = g0; g < g1; ++g) {
-    const uint32_t sa0 = sptr[(size_t)g * S * 64];
-    const uint32_t sa1 = GATE_UP ? sptr[(size_t)g * S * 64 + 64] : 0u;
-    v4i a0[4], a1[4];
-    v8i b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kt = g * 4 + u;
-      a0[u] = (v4i){0, 0, 0, 0};
-      a1[u] = (v4i){0, 0, 0, 0};
-      b[u] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-      if (kt < KT) {
-        a0[u] = *reinterpret_cast<const v4i*>(aptr + (size_t)kt * S * 1024);
-        if (GATE_UP) a1[u] = *reinterpret_cast<const v4i*>(aptr + (size_t)kt * S * 1024 + 1024);
-        if (valid) {
-          v4i lo = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64);
-          v4i hi = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64 + 32);
-          b[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      }
-    }
-    // padded K-tiles (kt >= KT) carry zero operands: they add exactly 0
-    acc0 = mfma_fp4_fp8<0>(a0[0], b[0], acc0, sa0, sb);
-    acc0 = mfma_fp4_fp8<1>(a0[1], b[1], acc0, sa0, sb);
-    acc0 = mfma_fp4_fp8<2>(a0[2], b[2], acc0, sa0, sb);
-    acc0 = mfma_fp4_fp8<3>(a0[3], b[3], acc0, sa0, sb);
-    if (GATE_UP) {
-      acc1 = mfma_fp4_fp8<0>(a1[0], b[0], acc1, sa1, sb);
-      acc1 = mfma_fp4_fp8<1>(a1[1], b[1], acc1, sa1, sb);
-      acc1 = mfma_fp4_fp8<2>(a1[2], b[2], acc1, sa1, sb);
-      acc1 = mfma_fp4_fp8<3>(a1[3], b[3], acc1, sa1, sb);
+#if DEC_DB
+  if (g0 < g1) {
+    Group<S> cur, nxt;
+    load_group<S>(cur, aptr, sptr, bptr, valid, g0, KT);
+    for (int g = g0; g < g1; ++g) {
+      if (g + 1 < g1) load_group<S>(nxt, aptr, sptr, bptr, valid, g + 1, KT);
+      mma_group<S>(cur, acc0, acc1, sb);
+      cur = nxt;
     }
   }
+#else
+  for (int g = g0; g < g1; ++g) {
+    Group<S> cur;
+    load_group<S>(cur, aptr, sptr, bptr, valid, g, KT);
+    mma_group<S>(cur, acc0, acc1, sb);
+  }
+#endif
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     red[wave][0][v][lane] = acc0[v];
-    if (GATE_UP) red[wave][S - 1][v][lane] = acc1[v];
+    if (S == 2) red[wave][S - 1][v][lane] = acc1[v];
   }
   __syncthreads();
+}
 
-  // thread t: lane l = t & 63 with (l & 31) < 16 (hi column of its slot), four v
+// Sum over waves (fixed order) of hi and lo columns for lane l (hi column,
+// l % 32 < 16), element v.
+template <int S>
+__device__ __forceinline__ float reduced(float (*red)[S][16][64], int s, int v, int l) {
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t = t + (red[w][s][v][l] + red[w][s][v][l + 16]);
+  return t;
+}
+
+__global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ x8,
+    const float* __restrict__ xs, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
+    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ a, int I,
+    int32_t* __restrict__ tile_ctr, uint8_t* __restrict__ aq8, float* __restrict__ as) {
+  __shared__ float red[NW][2][16][64];
+  __shared__ int last;
+  const int j = blockIdx.x, q = blockIdx.y;
+  if (q >= *n_tiles) return;
+  const int e = tile_expert[q];
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, part = c >> 4;
+  const int pair = sorted[q * DM + (c & 15)];
+  const bool valid = pair < P;
+  const int row = valid ? pair / top_k : 0;
+  decode_mainloop<2>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
+
+  // a = (g * sigmoid(g)) * u for the hi-column lanes' rows (waves 0..3)
   const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
-  if ((l & 31) >= 16) return;
-  const int oslot = l & 15;
-  const int op = q * 16 + oslot;
-  const int opair = sorted[op];
-  if (opair >= P) return;
-  const int orow = rows_are_tokens ? opair / top_k : op;
-  const float s = act_s[orow];
+  if ((l & 31) < 16 && vq < 4) {
+    const int op = q * DM + (l & 15);
+    const int opair = sorted[op];
+    if (opair < P) {
+      const float s = xs[opair / top_k];
 #pragma unroll
-  for (int vv = 0; vv < 4; ++vv) {
-    const int v = vq * 4 + vv;
-    const int n_local = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    float t0 = 0.0f, t1 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) t0 = t0 + (red[w][0][v][l] + red[w][0][v][l + 16]);
-    if (GATE_UP) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) t1 = t1 + (red[w][S - 1][v][l] + red[w][S - 1][v][l + 16]);
-      const float gg = s * t0, uu = s * t1;
-      const float a = (gg * moe::sigmoid_fixed(gg)) * uu;
-      out[(size_t)op * out_ld + j * 32 + n_local] = a;
-    } else {
-      out[(size_t)opair * out_ld + j * 32 + n_local] = s * t0;
+      for (int vv = 0; vv < 4; ++vv) {
+        const int v = vq * 4 + vv;
+        const int n = j * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        const float gg = s * reduced<2>(red, 0, v, l), uu = s * reduced<2>(red, 1, v, l);
+        moe::st_coherent(a + (size_t)op * I + n, (gg * moe::sigmoid_fixed(gg)) * uu);
+      }
     }
+  }
+  moe::release_wg();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = moe::counter_add(&tile_ctr[q], 1);
+    last = old == NT - 1;
+    if (last) tile_ctr[q] = 0;
+  }
+  __syncthreads();
+  if (!last) return;
+  moe::acquire_wg();
+  // requantize the tile's rows: one wave per row, loads in batches of 8
+  // values per lane (second pass re-reads from cache)
+  const int wave = threadIdx.x >> 6;
+  const int nv = I >> 6;  // values per lane, a multiple of 2
+  for (int slot = wave; slot < DM; slot += NW) {
+    const int p = q * DM + slot;
+    if (sorted[p] >= P) continue;
+    const float* arow = a + (size_t)p * I + lane;
+    uint8_t* dst = aq8 + (size_t)p * 2 * I + lane;
+    float amax = 0.f;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nv; u0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = moe::ld_coherent(arow + (size_t)min(u0 + u, nv - 1) * 64);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(v[u]));  // clamped repeats do not change the max
+    }
+    amax = moe::wave_max(amax);
+    const float s = amax / 127.0f;
+    if (lane == 0) as[p] = s;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nv; u0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = moe::ld_coherent(arow + (size_t)min(u0 + u, nv - 1) * 64);
+#pragma unroll 2
+      for (int u = 0; u < 8; ++u) {
+        if (u0 + u < nv) {
+          float qq = 0.f;
+          if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[u] / s), -127.f), 127.f);
+          int hi, lo;
+          moe::split_int8((int)qq, hi, lo);
+          dst[(size_t)(u0 + u) * 64] = (uint8_t)moe::small_int_to_e4m3(hi);
+          dst[I + (size_t)(u0 + u) * 64] = (uint8_t)moe::small_int_to_e4m3(lo);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * NW) void decode_down_kernel(
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ aq8,
+    const float* __restrict__ as, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
+    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ y, int H,
+    int32_t* __restrict__ tok_ctr, const float* __restrict__ w, float* __restrict__ out) {
+  __shared__ float red[NW][1][16][64];
+  __shared__ int done_tok[DM];
+  const int j = blockIdx.x, q = blockIdx.y;
+  if (q >= *n_tiles) return;
+  const int e = tile_expert[q];
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, part = c >> 4;
+  const int p = q * DM + (c & 15);
+  const bool valid = sorted[p] < P;
+  decode_mainloop<1>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
+
+  const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
+  if ((l & 31) < 16 && vq < 4) {
+    const int op = q * DM + (l & 15);
+    const int opair = sorted[op];
+    if (opair < P) {
+      const float s = as[op];
+      float* yrow = y + (size_t)opair * H + j * 32;
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int v = vq * 4 + vv;
+        moe::st_coherent(yrow + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), s * reduced<1>(red, 0, v, l));
+      }
+    }
+  }
+  moe::release_wg();
+  __syncthreads();
+  if (threadIdx.x < DM) {
+    const int opair = sorted[q * DM + threadIdx.x];
+    int t = -1;
+    if (opair < P) {
+      const int tok = opair / top_k;
+      const int old = moe::counter_add(&tok_ctr[(size_t)tok * NT + j], 1);
+      if (old == top_k - 1) {
+        tok_ctr[(size_t)tok * NT + j] = 0;
+        t = tok;
+      }
+    }
+    done_tok[threadIdx.x] = t;
+  }
+  __syncthreads();
+  moe::acquire_wg();
+  // combine the completed (token, column block) pairs: 16 slots x 32 columns
+  for (int idx = threadIdx.x; idx < DM * 32; idx += 64 * NW) {
+    const int t = done_tok[idx >> 5];
+    if (t < 0) continue;
+    const int n = j * 32 + (idx & 31);
+    float acc = 0.0f;
+    for (int jj = 0; jj < top_k; ++jj)
+      acc = __builtin_fmaf(w[(size_t)t * top_k + jj], moe::ld_coherent(y + ((size_t)t * top_k + jj) * H + n), acc);
+    out[(size_t)t * H + n] = acc;
   }
 }
 
 }  // namespace
 
-hipError_t moe_k_decode_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act8,
-                             const float* act_s, const int32_t* sorted, const int32_t* tile_expert,
-                             const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
-                             int rows_are_tokens, float* out, int out_ld, hipStream_t st) {
+int moe_k_decode_block_m() { return DM; }
+
+hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
+                                const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
+                                int max_tiles, int H, int I, int top_k, int P, float* a, int32_t* tile_ctr,
+                                uint8_t* aq8, float* as, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
-  dim3 grid(NT, max_tiles);
-  if (gate_up)
-    decode_gemm_kernel<true><<<grid, 256, 0, st>>>(wq, wsc, act8, act_s, sorted, tile_expert, n_tiles, K, NT, top_k,
-                                                   P, rows_are_tokens, out, out_ld);
-  else
-    decode_gemm_kernel<false><<<grid, 256, 0, st>>>(wq, wsc, act8, act_s, sorted, tile_expert, n_tiles, K, NT, top_k,
-                                                    P, rows_are_tokens, out, out_ld);
+  dim3 grid(I / 32, max_tiles);
+  decode_gate_up_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32, top_k, P, a,
+                                              I, tile_ctr, aq8, as);
+  return hipGetLastError();
+}
+
+hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
+                             const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
+                             int H, int I, int top_k, int P, float* y, int32_t* tok_ctr, const float* w, float* out,
+                             hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+  dim3 grid(H / 32, max_tiles);
+  decode_down_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32, top_k, P, y, H,
+                                           tok_ctr, w, out);
   return hipGetLastError();
 }

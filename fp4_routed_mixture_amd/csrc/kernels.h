@@ -13,17 +13,19 @@ hipError_t moe_k_unpack(int which, int E, int N, int K, const uint8_t* pcodes, c
                         uint8_t* codes, uint8_t* scales, hipStream_t st);
 
 // route.hip
-hipError_t moe_k_router_logits(int x_dtype, const void* x, const float* wr, const float* bias, float* logits,
-                               int T, int H, int E, hipStream_t st);
-hipError_t moe_k_router_logits_variant(int variant, int x_dtype, const void* x, const float* wr, const float* bias,
-                                       float* logits, int T, int H, int E, hipStream_t st);
-hipError_t moe_k_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t st);
+int moe_k_router_slices(int T, int H);
+size_t moe_k_router_partial_bytes(int T, int H, int E);
+hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
+                                hipStream_t st);
+hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
+                            int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
+                            hipStream_t st);
 
 // sort.hip
 size_t moe_k_sort_scratch_bytes(int P, int E);
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      hipStream_t st);
+                      int32_t* counters, int n_counters, hipStream_t st);
 
 // quant.hip
 hipError_t moe_k_quant_int8(int in_dtype, const void* v, int rows, int K, int out_fp8pair, void* q, float* scales,
@@ -36,10 +38,15 @@ hipError_t moe_k_gather_rows(const void* src, int row_bytes, const int32_t* row_
                              hipStream_t st);
 
 // gemm_decode.hip
-hipError_t moe_k_decode_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act8,
-                             const float* act_s, const int32_t* sorted, const int32_t* tile_expert,
-                             const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
-                             int rows_are_tokens, float* out, int out_ld, hipStream_t st);
+int moe_k_decode_block_m();
+hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
+                                const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
+                                int max_tiles, int H, int I, int top_k, int P, float* a, int32_t* tile_ctr,
+                                uint8_t* aq8, float* as, hipStream_t st);
+hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
+                             const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
+                             int H, int I, int top_k, int P, float* y, int32_t* tok_ctr, const float* w, float* out,
+                             hipStream_t st);
 
 // gemm_prefill.hip
 int moe_k_prefill_block_m();

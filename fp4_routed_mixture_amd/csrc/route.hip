@@ -1,42 +1,46 @@
-// Sigmoid-score top-k router.
+// Sigmoid-score top-k router, and the fused kernels that finish routing.
 //
 // Logits use one fixed fp32 order so that every implementation produces the
 // same bits (the routing ids must match exactly): H splits into 64 contiguous
 // chunks of L = H/64; chunk c is the fused-multiply-add chain over ascending k
 // from 0; the 64 chunk sums are added as a perfect pairwise tree in index
-// order; the bias is added last. Two kernels produce identical bits:
-//   * router_wave: one wave per expert, lane c owns chunk c, the tree is an
-//     xor-butterfly across lanes (xor 1 pairs chunks 2j and 2j+1, xor 2 pairs
-//     those pairs, ...). Used for small token counts, where streaming Wr once
-//     at full bandwidth is what matters.
-//   * router_tiled: 64 tokens x 64 experts per workgroup, 4x4 per thread,
-//     operands staged through LDS; each thread keeps a 6-slot pairwise stack
-//     per output, pushing a chunk sum whenever a chunk ends (the carry chain
-//     of a binary counter reproduces the pairwise tree exactly).
-// Top-k: one wave per token; scores s = 1/(1 + exp(-l)); k rounds of a wave
-// argmax keyed (score desc, expert asc); w_j = s_j / S with S accumulated
-// left to right in slot order.
+// order; the bias is added last.
+//
+// router_partial: the 64 chunks form 8 slices of 8 chunks. A workgroup
+// computes a (tokens x experts) tile over one slice, staging both operands
+// through LDS; each thread owns an RA x RB block of outputs and keeps a
+// 3-level pairwise stack per output, pushing a chunk sum whenever a chunk
+// ends (the carry chain of a binary counter reproduces the tree exactly).
+// The slice sums (tree level 3) go to partial[8][T][E]; the kernels below add
+// the top three levels, ((S0+S1)+(S2+S3)) + ((S4+S5)+(S6+S7)), then the bias.
+//
+// Top-k: scores s = 1/(1 + exp(-l)); k rounds of a wave argmax keyed (score
+// desc, expert asc); w_j = s_j / S with S accumulated left to right in slot
+// order.
+//
+// Small batches (T <= 64) keep all 64 chunk sums (one chunk per workgroup, so
+// each workgroup loads its operands once) and finish the whole tree in
+// topk_quant_token, one workgroup per token, which also quantizes the token's
+// row of x. Larger batches keep 8 slice sums; topk_quant uses one wave per
+// token.
 #include "common.h"
 #include "kernels.h"
+#include "sort_dev.h"
 
 namespace {
 
-template <typename XT>
-__device__ __forceinline__ float load_x(const XT* p);
-template <>
-__device__ __forceinline__ float load_x<float>(const float* p) { return *p; }
-template <>
-__device__ __forceinline__ float load_x<uint16_t>(const uint16_t* p) { return moe::bf16_bits_to_f32(*p); }
+constexpr int NSLICE = 8;
+constexpr int RKS = 32;  // k per LDS stage
 
 template <typename XT>
-__device__ __forceinline__ void load_x4(const XT* p, float* o);
+__device__ __forceinline__ void load4(const XT* p, float* o);
 template <>
-__device__ __forceinline__ void load_x4<float>(const float* p, float* o) {
+__device__ __forceinline__ void load4<float>(const float* p, float* o) {
   float4 v = *reinterpret_cast<const float4*>(p);
   o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
 }
 template <>
-__device__ __forceinline__ void load_x4<uint16_t>(const uint16_t* p, float* o) {
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* o) {
   uint2 v = *reinterpret_cast<const uint2*>(p);
   o[0] = __uint_as_float(v.x << 16);
   o[1] = __uint_as_float(v.x & 0xffff0000u);
@@ -44,211 +48,415 @@ __device__ __forceinline__ void load_x4<uint16_t>(const uint16_t* p, float* o) {
   o[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
-// ---------------------------------------------------------------------------
-// One wave per expert; 4 experts per 256-thread workgroup.
-// ---------------------------------------------------------------------------
 template <typename XT>
-__global__ __launch_bounds__(256) void router_wave_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
-                                                          const float* __restrict__ bias, float* __restrict__ logits,
-                                                          int T, int H, int E) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int c = threadIdx.x & 63;
-  if (e >= E) return;
+__device__ __forceinline__ float load1(const XT* p);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return moe::bf16_bits_to_f32(*p); }
+
+// ---------------------------------------------------------------------------
+// Partial logits over one H slice. 256 threads = 16 x 16; tile (16 RA) tokens
+// x (16 RB) experts; KS k values per LDS stage; the next stage's global loads
+// are in flight while the current stage is computed.
+// ---------------------------------------------------------------------------
+template <typename XT, int RA, int RB, int KS, int CPS>
+__global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
+                                                             float* __restrict__ partial, int T, int H, int E) {
+  static_assert(CPS == 1 || CPS == 8, "chunks per slice");
+  constexpr int TT = 16 * RA, TE = 16 * RB;
+  constexpr int NX = TT * KS / 4 / 256, NW = TE * KS / 4 / 256;  // float4 groups per thread
+  static_assert(NX >= 1 && NW >= 1, "tile too small for the stage");
+  __shared__ float xs[KS][TT + 1];
+  __shared__ float ws[KS][TE + 1];
+  const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, slice = blockIdx.z;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int L = H >> 6;
-  const float* wrow = wr + (size_t)e * H + (size_t)c * L;
-  const float b = bias ? bias[e] : 0.0f;
-  for (int t = 0; t < T; ++t) {
-    const XT* xrow = x + (size_t)t * H + (size_t)c * L;
-    float p = 0.0f;
-    for (int i = 0; i < L; i += 4) {
-      float xv[4];
-      load_x4<XT>(xrow + i, xv);
-      float4 wv = *reinterpret_cast<const float4*>(wrow + i);
-      p = __builtin_fmaf(xv[0], wv.x, p);
-      p = __builtin_fmaf(xv[1], wv.y, p);
-      p = __builtin_fmaf(xv[2], wv.z, p);
-      p = __builtin_fmaf(xv[3], wv.w, p);
+  const int kbeg = slice * CPS * L, kend = kbeg + CPS * L;
+
+  float acc[RA][RB], st0[RA][RB], st1[RA][RB], st2[RA][RB];
+#pragma unroll
+  for (int a = 0; a < RA; ++a)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) { acc[a][b] = 0.f; st0[a][b] = 0.f; st1[a][b] = 0.f; st2[a][b] = 0.f; }
+
+  float xr[NX][4], wrr[NW][4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int n = 0; n < NX; ++n) {
+      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
+      xr[n][0] = xr[n][1] = xr[n][2] = xr[n][3] = 0.f;
+      if (t0 + r < T) load4<XT>(x + (size_t)(t0 + r) * H + k0 + kq, xr[n]);
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) p = p + __shfl_xor(p, o, 64);
-    if (c == 0) logits[(size_t)t * E + e] = bias ? p + b : p;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 64x64 tile per workgroup, 16x16 threads with 4x4 outputs each.
-// ---------------------------------------------------------------------------
-constexpr int RT = 64;   // tokens per tile
-constexpr int RE = 64;   // experts per tile
-constexpr int RK = 32;   // k per LDS stage
-
-template <typename XT>
-__global__ __launch_bounds__(256) void router_tiled_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
-                                                           const float* __restrict__ bias, float* __restrict__ logits,
-                                                           int T, int H, int E) {
-  __shared__ float xs[RK][RT + 4];
-  __shared__ float ws[RK][RE + 4];
-  const int t0 = blockIdx.y * RT, e0 = blockIdx.x * RE;
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int L = H >> 6;
-
-  float acc[4][4];
-  float st[6][4][4];
+    for (int n = 0; n < NW; ++n) {
+      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e0 + r < E) v = *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + k0 + kq);
+      wrr[n][0] = v.x; wrr[n][1] = v.y; wrr[n][2] = v.z; wrr[n][3] = v.w;
+    }
+  };
+  auto stash = [&]() {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int n = 0; n < NX; ++n) {
+      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+      for (int u = 0; u < 4; ++u) xs[kq + u][r] = xr[n][u];
+    }
+#pragma unroll
+    for (int n = 0; n < NW; ++n) {
+      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ws[kq + u][r] = wrr[n][u];
+    }
+  };
 
-  // staging map: 64 rows x 32 k = 512 groups of 4 k; 2 groups per thread
   int chunk = 0, in_chunk = 0;
-  for (int k0 = 0; k0 < H; k0 += RK) {
+  fetch(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += KS) {
     __syncthreads();
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      int gidx = tid + rep * 256;
-      int r = gidx >> 3, kq = (gidx & 7) * 4;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t0 + r < T) load_x4<XT>(x + (size_t)(t0 + r) * H + k0 + kq, v);
-      xs[kq + 0][r] = v[0]; xs[kq + 1][r] = v[1]; xs[kq + 2][r] = v[2]; xs[kq + 3][r] = v[3];
-      float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + r < E) w4 = *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + k0 + kq);
-      ws[kq + 0][r] = w4.x; ws[kq + 1][r] = w4.y; ws[kq + 2][r] = w4.z; ws[kq + 3][r] = w4.w;
-    }
+    stash();
     __syncthreads();
-    for (int kk = 0; kk < RK; ++kk) {
-      float4 xv = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
-      float4 wv = *reinterpret_cast<const float4*>(&ws[kk][tx * 4]);
-      float xa[4] = {xv.x, xv.y, xv.z, xv.w};
-      float wa[4] = {wv.x, wv.y, wv.z, wv.w};
+    if (k0 + KS < kend) fetch(k0 + KS);
+#pragma unroll 4
+    for (int kk = 0; kk < KS; ++kk) {
+      float xa[RA], wb[RB];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < RA; ++a) xa[a] = xs[kk][ty * RA + a];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xa[a], wa[b], acc[a][b]);
+      for (int b = 0; b < RB; ++b) wb[b] = ws[kk][tx * RB + b];
+#pragma unroll
+      for (int a = 0; a < RA; ++a)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[a][b] = __builtin_fmaf(xa[a], wb[b], acc[a][b]);
       if (++in_chunk == L) {
-        // push the finished chunk sums onto the pairwise stack
         in_chunk = 0;
+        // push the chunk sums: chunk index within the slice = 3-bit counter
+        const bool b0 = chunk & 1, b1 = chunk & 2, b2 = chunk & 4;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < RA; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
+          for (int b = 0; b < RB; ++b) {
             float v = acc[a][b];
-            acc[a][b] = 0.0f;
-#pragma unroll
-            for (int lv = 0; lv < 6; ++lv) {
-              if ((chunk >> lv) & 1) {
-                v = st[lv][a][b] + v;
+            acc[a][b] = 0.f;
+            if (CPS == 1) {
+              st2[a][b] = v;  // the chunk sum itself (tree level 0)
+            } else if (!b0) {
+              st0[a][b] = v;
+            } else {
+              v = st0[a][b] + v;
+              if (!b1) {
+                st1[a][b] = v;
               } else {
-                st[lv][a][b] = v;
-                break;
+                v = st1[a][b] + v;
+                if (!b2) st2[a][b] = v;
+                else st2[a][b] = st2[a][b] + v;  // chunk 7: the slice total
               }
             }
-            if (chunk == 63) st[0][a][b] = v;  // the full tree sum
           }
         ++chunk;
       }
     }
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    int t = t0 + ty * 4 + a;
+  for (int a = 0; a < RA; ++a) {
+    const int t = t0 + ty * RA + a;
     if (t >= T) continue;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int e = e0 + tx * 4 + b;
-      if (e < E) logits[(size_t)t * E + e] = bias ? st[0][a][b] + bias[e] : st[0][a][b];
+    for (int b = 0; b < RB; ++b) {
+      const int e = e0 + tx * RB + b;
+      if (e < E) partial[((size_t)slice * T + t) * E + e] = st2[a][b];
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Top-k + renormalization: one wave per token, 4 tokens per workgroup.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  constexpr int MAXPER = 16;  // E <= 1024
-  float s[MAXPER];
-  const int per = (E + 63) / 64;
+// Logit of (t, e): the remaining tree levels over the NS slice sums (a
+// perfect pairwise tree in index order), then the bias.
+template <int NS>
+__device__ __forceinline__ float finish_logit(const float* __restrict__ partial, const float* __restrict__ bias, int T,
+                                              int E, int t, int e) {
+  const size_t st = (size_t)T * E, o = (size_t)t * E + e;
+  float v[NS];
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    int e = lane + 64 * i;
-    s[i] = (i < per && e < E) ? moe::sigmoid_fixed(logits[(size_t)t * E + e]) : -1.0f;  // sigmoid >= 0
+  for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
+#pragma unroll
+  for (int w = NS; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  return bias ? v[0] + bias[e] : v[0];
+}
+
+// Quantize one row of x with one wave: int8 as FP8 (hi, lo) planes
+// [2][K] + fp32 scale, or MXFP4 codes [K/2] + E8M0 scales [K/32]
+// (K % 256 == 0). Compact loops: four four-element units per lane per batch.
+template <typename XT>
+__device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K, int mx, uint8_t* __restrict__ q,
+                                            uint8_t* __restrict__ qs) {
+  const int lane = threadIdx.x & 63;
+  if (!mx) {
+    const int nu = K >> 8;  // four-element units per lane
+    float amax = 0.f;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nu; u0 += 4) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u0 + u, nu - 1) * 64 + lane) * 4, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+    }
+    amax = moe::wave_max(amax);
+    const float s = amax / 127.0f;
+    if (lane == 0) *reinterpret_cast<float*>(qs) = s;
+#pragma unroll 1
+    for (int u = 0; u < nu; ++u) {
+      float v[4];
+      const size_t i = ((size_t)u * 64 + lane) * 4;
+      load4<XT>(row + i, v);
+      uint32_t hw = 0, lw = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float qq = 0.f;
+        if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
+        int hi, lo;
+        moe::split_int8((int)qq, hi, lo);
+        hw |= moe::small_int_to_e4m3(hi) << (8 * m);
+        lw |= moe::small_int_to_e4m3(lo) << (8 * m);
+      }
+      *reinterpret_cast<uint32_t*>(q + i) = hw;
+      *reinterpret_cast<uint32_t*>(q + K + i) = lw;
+    }
+  } else {
+#pragma unroll 1
+    for (int b = lane; b < K / 32; b += 64) {
+      float v[32];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) load4<XT>(row + b * 32 + i, v + i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = amax > 0.f ? moe::mx_scale_exp(amax) : 0;
+      uint32_t w[4] = {0, 0, 0, 0};
+      if (amax > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float vs = __builtin_ldexpf(v[i], 127 - e);
+          const uint32_t c = moe::e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
+          w[i / 8] |= c << ((i % 8) * 4);
+        }
+      }
+      *reinterpret_cast<uint4*>(q + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      qs[b] = (uint8_t)e;
+    }
   }
+}
+
+// k rounds of a wave argmax over s[i] = score of expert lane + 64 i, keyed
+// (score desc, expert asc). Sigmoid scores are >= 0; -1 marks experts that do
+// not exist. Lane j (< K) returns slot j: its expert in *id, its renormalized
+// weight in *w (S accumulated left to right over the slots).
+__device__ __forceinline__ void wave_select(const float (&s)[16], int K, int* id, float* w) {
+  const int lane = threadIdx.x & 63;
   uint32_t taken = 0;
-  float ssel[16];
-  int isel[16];
+  float my_s = 0.f;
+  int my_id = 0;
+#pragma unroll 1
   for (int j = 0; j < K; ++j) {
-    // lane-local best: highest score, lowest index (i ascending = e ascending)
     float bv = -2.0f;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < MAXPER; ++i) {
-      int e = lane + 64 * i;
-      if (!((taken >> i) & 1) && s[i] > bv) { bv = s[i]; bi = e; }
-    }
-    // wave argmax
+    for (int i = 0; i < 16; ++i)
+      if (!((taken >> i) & 1) && s[i] > bv) { bv = s[i]; bi = lane + 64 * i; }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    ssel[j] = bv;
-    isel[j] = bi;
+    if (lane == j) { my_s = bv; my_id = bi; }
   }
-  if (lane == 0) {
-    float S = 0.0f;
-    for (int j = 0; j < K; ++j) S = S + ssel[j];
-    for (int j = 0; j < K; ++j) {
-      ids[(size_t)t * K + j] = isel[j];
-      w[(size_t)t * K + j] = (S == 0.0f) ? 1.0f / (float)K : ssel[j] / S;
+  float S = 0.0f;
+#pragma unroll 1
+  for (int j = 0; j < K; ++j) S = S + __shfl(my_s, j, 64);
+  *id = my_id;
+  *w = (S == 0.0f) ? 1.0f / (float)K : my_s / S;
+}
+
+// Top-k of one token from its scores in LDS, by one wave.
+__device__ __forceinline__ void wave_topk_lds(const float* __restrict__ sc, int E, int K, int* id, float* wv) {
+  const int lane = threadIdx.x & 63;
+  float s[16];  // E <= 1024
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    s[i] = e < E ? sc[e] : -1.0f;
+  }
+  wave_select(s, K, id, wv);
+}
+
+// ---------------------------------------------------------------------------
+// Small batches: one 256-thread workgroup per token. Threads finish the
+// logits of the token's experts from the 64 chunk sums (the whole pairwise
+// tree), the sigmoid scores go to LDS, wave 0 selects the top k, and all
+// four waves quantize the token's row of x (int8 rows only).
+// ---------------------------------------------------------------------------
+template <typename XT>
+__global__ __launch_bounds__(256) void topk_quant_token_kernel(const float* __restrict__ partial,
+                                                               const float* __restrict__ bias, const XT* __restrict__ x,
+                                                               int T, int H, int E, int K, int quant, int mx,
+                                                               int32_t* __restrict__ ids_out,
+                                                               float* __restrict__ w_out, uint8_t* __restrict__ xq,
+                                                               uint8_t* __restrict__ xs) {
+  __shared__ float sc[1024];
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 256) sc[e] = moe::sigmoid_fixed(finish_logit<64>(partial, bias, T, E, t, e));
+  __syncthreads();
+  if (wave == 0) {
+    float s[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = lane + 64 * i < E ? sc[lane + 64 * i] : -1.0f;
+    int id;
+    float wv;
+    wave_select(s, K, &id, &wv);
+    if (lane < K) {
+      ids_out[(size_t)t * K + lane] = id;
+      w_out[(size_t)t * K + lane] = wv;
     }
   }
+  if (!quant) return;
+  const XT* row = x + (size_t)t * H;
+  if (mx) {
+    if (wave == 1) wave_quant_row<XT>(row, H, 1, xq + (size_t)t * (H / 2), xs + (size_t)t * (H / 32));
+    return;
+  }
+  // int8 row: every thread holds H/256 values (H % 256 == 0), loads issued together
+  const int nu = H >> 10;  // four-element units per thread
+  float amax = 0.f;
+  for (int u0 = 0; u0 < nu; u0 += 4) {
+    float v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u0 + u, nu - 1) * 256 + tid) * 4, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+  }
+  // H not a multiple of 1024: the remaining 256-element units
+  for (int i = nu * 1024 + tid * 4; i < H; i += 1024) {
+    float v[4];
+    load4<XT>(row + i, v);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  amax = moe::wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  if (tid == 0) reinterpret_cast<float*>(xs)[t] = s;
+  uint8_t* q = xq + (size_t)t * 2 * H;
+  for (int i = tid * 4; i < H; i += 1024) {
+    float v[4];
+    load4<XT>(row + i, v);
+    uint32_t hw = 0, lw = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float qq = 0.f;
+      if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
+      int hi, lo;
+      moe::split_int8((int)qq, hi, lo);
+      hw |= moe::small_int_to_e4m3(hi) << (8 * m);
+      lw |= moe::small_int_to_e4m3(lo) << (8 * m);
+    }
+    *reinterpret_cast<uint32_t*>(q + i) = hw;
+    *reinterpret_cast<uint32_t*>(q + H + i) = lw;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One wave per token: top-k and (optionally) the quantization of the token.
+// ---------------------------------------------------------------------------
+template <typename XT>
+__global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict__ partial,
+                                                         const float* __restrict__ bias, const XT* __restrict__ x,
+                                                         int T, int H, int E, int K, int quant, int mx,
+                                                         int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                                         uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  __shared__ float sc[4][1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+#pragma unroll 1
+  for (int e = lane; e < E; e += 64) sc[wave][e] = moe::sigmoid_fixed(finish_logit<8>(partial, bias, T, E, t, e));
+  int id;
+  float wv;
+  wave_topk_lds(sc[wave], E, K, &id, &wv);
+  if (lane < K) {
+    ids_out[(size_t)t * K + lane] = id;
+    w_out[(size_t)t * K + lane] = wv;
+  }
+  if (quant) {
+    const size_t qrow = mx ? (size_t)H / 2 : (size_t)2 * H;
+    const size_t srow = mx ? (size_t)H / 32 : 4;
+    wave_quant_row<XT>(x + (size_t)t * H, H, mx, xq + (size_t)t * qrow, xs + (size_t)t * srow);
+  }
+}
+
+template <typename XT>
+hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, hipStream_t st) {
+  const int L = H / 64;  // chunk length, a multiple of 4
+  if (T <= 64 && L % 64 == 0 && L <= 256) {
+    // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range
+    if (T <= 16) {
+      dim3 grid((E + 15) / 16, 1, 64);
+      router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+    } else {
+      dim3 grid((E + 15) / 16, 1, 64);
+      router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+    }
+  } else {
+    dim3 grid((E + 63) / 64, (T + 63) / 64, 8);
+    router_partial_kernel<XT, 4, 4, 32, 8><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t moe_k_router_logits(int x_dtype, const void* x, const float* wr, const float* bias, float* logits,
-                               int T, int H, int E, hipStream_t st) {
-  if (T <= 64) {
-    dim3 grid((E + 3) / 4);
-    if (x_dtype == 0)
-      router_wave_kernel<float><<<grid, 256, 0, st>>>((const float*)x, wr, bias, logits, T, H, E);
-    else
-      router_wave_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, wr, bias, logits, T, H, E);
-  } else {
-    dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
-    if (x_dtype == 0)
-      router_tiled_kernel<float><<<grid, 256, 0, st>>>((const float*)x, wr, bias, logits, T, H, E);
-    else
-      router_tiled_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, wr, bias, logits, T, H, E);
-  }
-  return hipGetLastError();
+int moe_k_router_slices(int T, int H) {
+  const int L = H / 64;
+  return (T <= 64 && L % 64 == 0 && L <= 256) ? 64 : 8;
 }
 
-hipError_t moe_k_router_logits_variant(int variant, int x_dtype, const void* x, const float* wr, const float* bias,
-                                       float* logits, int T, int H, int E, hipStream_t st) {
-  if (variant == 0) {
-    dim3 grid((E + 3) / 4);
-    if (x_dtype == 0)
-      router_wave_kernel<float><<<grid, 256, 0, st>>>((const float*)x, wr, bias, logits, T, H, E);
-    else
-      router_wave_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, wr, bias, logits, T, H, E);
-  } else {
-    dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
-    if (x_dtype == 0)
-      router_tiled_kernel<float><<<grid, 256, 0, st>>>((const float*)x, wr, bias, logits, T, H, E);
-    else
-      router_tiled_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, wr, bias, logits, T, H, E);
-  }
-  return hipGetLastError();
+size_t moe_k_router_partial_bytes(int T, int H, int E) { return (size_t)moe_k_router_slices(T, H) * T * E * 4; }
+
+hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
+                                hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (x_dtype == 0) return launch_partial<float>((const float*)x, wr, partial, T, H, E, st);
+  return launch_partial<uint16_t>((const uint16_t*)x, wr, partial, T, H, E, st);
 }
 
-hipError_t moe_k_topk(const float* logits, int T, int E, int K, int32_t* ids, float* w, hipStream_t st) {
-  topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, K, ids, w);
+hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
+                            int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
+                            hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (moe_k_router_slices(T, H) == 64) {
+    // per-token workgroups
+    if (x_dtype == 0)
+      topk_quant_token_kernel<float><<<T, 256, 0, st>>>(partial, bias, (const float*)x, T, H, E, K, quant, mx, ids, w,
+                                                        xq, xs);
+    else
+      topk_quant_token_kernel<uint16_t><<<T, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H, E, K, quant, mx,
+                                                           ids, w, xq, xs);
+    return hipGetLastError();
+  }
+  const int blocks = (T + 3) / 4;
+  if (x_dtype == 0)
+    topk_quant_kernel<float><<<blocks, 256, 0, st>>>(partial, bias, (const float*)x, T, H, E, K, quant, mx, ids, w, xq,
+                                                     xs);
+  else
+    topk_quant_kernel<uint16_t><<<blocks, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H, E, K, quant, mx, ids,
+                                                        w, xq, xs);
   return hipGetLastError();
 }

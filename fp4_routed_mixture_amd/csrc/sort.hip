@@ -16,107 +16,29 @@
 // bases, tiles, padding sentinels) -> sort_scatter.
 #include "common.h"
 #include "kernels.h"
+#include "sort_dev.h"
 
 namespace {
 
-constexpr int SB = 1024;  // pairs per block
 
-// Stable rank of each lane's id among lanes of this wave with the same id,
-// and (for the lane that is lowest in its group) the group size.
-__device__ __forceinline__ void wave_match_rank(int id, bool valid, int& rank, int& group_count, bool& leader) {
-  const int lane = threadIdx.x & 63;
-  uint64_t active = __ballot(valid);
-  rank = 0;
-  group_count = 0;
-  leader = false;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  while (active) {
-    int first = __ffsll((unsigned long long)active) - 1;
-    int fid = __shfl(id, first, 64);
-    uint64_t m = __ballot(valid && id == fid);
-    if (valid && id == fid) {
-      rank = __popcll(m & below);
-      group_count = __popcll(m);
-      leader = lane == first;
-    }
-    active &= ~m;
-  }
-}
-
-// Per block of SB pairs: local stable rank of each pair and per-expert counts.
-// wcnt: LDS [16 waves][E]
-__device__ void block_rank(const int32_t* __restrict__ ids, int P, int E, int base, int* wcnt, int& my_rank,
-                           int& my_id, bool& my_valid) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
-  __syncthreads();
-  const int i = base + tid;
-  my_valid = i < P;
-  my_id = my_valid ? ids[i] : 0;
-  int rank, cnt;
-  bool leader;
-  wave_match_rank(my_id, my_valid, rank, cnt, leader);
-  if (leader) wcnt[wave * E + my_id] = cnt;
-  __syncthreads();
-  // exclusive prefix over waves, per expert (in place), then local rank
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < 16; ++w) {
-      int c = wcnt[w * E + e];
-      wcnt[w * E + e] = run;
-      run += c;
-    }
-    wcnt[16 * E + e] = run;  // block total for e
-  }
-  __syncthreads();
-  my_rank = my_valid ? wcnt[wave * E + my_id] + rank : 0;
-}
-
-// Block-wide exclusive scan of padded counts over E experts (E <= 1024,
-// 1024 threads): writes offsets[0..E].
-__device__ void scan_offsets(const int* counts_lds, int E, int block_m, int* offs_lds, int* tmp) {
-  const int tid = threadIdx.x;
-  int v = 0;
-  if (tid < E) v = (counts_lds[tid] + block_m - 1) / block_m * block_m;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
-  }
-  if (tid < E) offs_lds[tid + 1] = tmp[tid];
-  if (tid == 0) offs_lds[0] = 0;
-  __syncthreads();
-}
-
-__device__ void write_tiles_and_padding(const int* counts, const int* offs, int E, int P, int block_m,
-                                        int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
-                                        int32_t* __restrict__ n_tiles) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
-    for (int p = offs[e] + counts[e]; p < offs[e + 1]; ++p) sorted[p] = P;
-    for (int q = offs[e] / block_m; q < offs[e + 1] / block_m; ++q) tile_expert[q] = e;
-  }
-  if (tid == 0) *n_tiles = offs[E] / block_m;
-}
-
-// P <= SB: everything in one workgroup.
+// P <= moe::SB: everything in one workgroup.
 __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m,
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
                                                           int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ n_tiles) {
+                                                          int32_t* __restrict__ n_tiles,
+                                                          int32_t* __restrict__ counters, int n_counters) {
   extern __shared__ int smem[];
+  for (int i = threadIdx.x; i < n_counters; i += 1024) counters[i] = 0;
   int* wcnt = smem;                  // 17 * E
   int* offs = wcnt + 17 * E;         // E + 1
   int* tmp = offs + E + 1;           // 1024
-  int rank, id;
-  bool valid;
-  block_rank(ids, P, E, 0, wcnt, rank, id, valid);
+  const bool valid = (int)threadIdx.x < P;
+  const int id = valid ? ids[threadIdx.x] : 0;
+  int rank;
+  moe::block_rank(id, valid, E, wcnt, rank);
   const int* tot = wcnt + 16 * E;
-  scan_offsets(tot, E, block_m, offs, tmp);
+  moe::scan_offsets(tot, E, block_m, offs, tmp);
   const int tid = threadIdx.x;
   if (valid) {
     int p = offs[id] + rank;
@@ -125,7 +47,7 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
   }
   for (int e = tid; e < E; e += blockDim.x) counts[e] = tot[e];
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
-  write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+  moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
 }
 
 // Large P, step 1: per block local ranks and per-expert block counts.
@@ -133,10 +55,11 @@ __global__ __launch_bounds__(1024) void sort_count_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ local_rank,
                                                           int32_t* __restrict__ block_hist) {
   extern __shared__ int smem[];
-  int rank, id;
-  bool valid;
-  block_rank(ids, P, E, blockIdx.x * SB, smem, rank, id, valid);
-  const int i = blockIdx.x * SB + threadIdx.x;
+  const int i = blockIdx.x * moe::SB + threadIdx.x;
+  const bool valid = i < P;
+  const int id = valid ? ids[i] : 0;
+  int rank;
+  moe::block_rank(id, valid, E, smem, rank);
   if (valid) local_rank[i] = rank;
   for (int e = threadIdx.x; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = smem[16 * E + e];
 }
@@ -148,8 +71,10 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted,
                                                          int32_t* __restrict__ tile_expert,
-                                                         int32_t* __restrict__ n_tiles) {
+                                                         int32_t* __restrict__ n_tiles,
+                                                         int32_t* __restrict__ counters, int n_counters) {
   extern __shared__ int smem[];
+  for (int i = threadIdx.x; i < n_counters; i += 1024) counters[i] = 0;
   int* tot = smem;            // E
   int* offs = tot + E;        // E + 1
   int* tmp = offs + E + 1;    // 1024
@@ -164,13 +89,13 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
     tot[e] = run;
   }
   __syncthreads();
-  scan_offsets(tot, E, block_m, offs, tmp);
+  moe::scan_offsets(tot, E, block_m, offs, tmp);
   for (int e = tid; e < E; e += blockDim.x) {
     counts[e] = tot[e];
     for (int b = 0; b < nblocks; ++b) block_hist[(size_t)b * E + e] += offs[e];
   }
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
-  write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+  moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
 }
 
 // Large P, step 3: scatter.
@@ -180,7 +105,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ sorted, int32_t* __restrict__ pos) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= P) return;
-  const int b = i / SB;
+  const int b = i / moe::SB;
   const int p = block_base[(size_t)b * E + ids[i]] + local_rank[i];
   sorted[p] = i;
   pos[i] = p;
@@ -189,14 +114,14 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 }  // namespace
 
 size_t moe_k_sort_scratch_bytes(int P, int E) {
-  if (P <= SB) return 0;
-  size_t nb = (P + SB - 1) / SB;
+  if (P <= moe::SB) return 0;
+  size_t nb = (P + moe::SB - 1) / moe::SB;
   return ((size_t)P * 4 + 255) / 256 * 256 + (nb * E * 4 + 255) / 256 * 256;
 }
 
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      hipStream_t st) {
+                      int32_t* counters, int n_counters, hipStream_t st) {
   // gfx950 has 160 KB of LDS per workgroup; above 64 KB a kernel must opt in
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
@@ -208,19 +133,21 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
     if (e2 != hipSuccess) return e2;
     lds_opt_in = true;
   }
-  if (P <= SB) {
+  if (P <= moe::SB) {
     size_t lds = (size_t)(17 * E + E + 1 + 1024) * 4;
-    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles);
+    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles,
+                                            counters, n_counters);
     return hipGetLastError();
   }
-  int nb = (P + SB - 1) / SB;
+  int nb = (P + moe::SB - 1) / moe::SB;
   int32_t* local_rank = (int32_t*)scratch;
   int32_t* block_hist = (int32_t*)((char*)scratch + ((size_t)P * 4 + 255) / 256 * 256);
   sort_count_kernel<<<nb, 1024, (size_t)17 * E * 4, st>>>(ids, P, E, local_rank, block_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, 1024, (size_t)(E + E + 1 + 1024) * 4, st>>>(nb, P, E, block_m, block_hist, counts, offsets,
-                                                                    sorted, tile_expert, n_tiles);
+                                                                    sorted, tile_expert, n_tiles, counters,
+                                                                    n_counters);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scatter_kernel<<<(P + 255) / 256, 256, 0, st>>>(ids, P, E, local_rank, block_hist, sorted, pos);
