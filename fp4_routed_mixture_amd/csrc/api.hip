@@ -43,9 +43,8 @@ int check_shape(const moe_config* c) {
 
 // Workspace plan of one layer call.
 struct Plan {
-  int block_m, P, cap, max_tiles, n_counters;
-  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, counters, a, aq, as, y,
-      total;
+  int block_m, P, cap, max_tiles;
+  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, a, aq, as, y, total;
 };
 
 Plan make_plan(const moe_config* c) {
@@ -74,10 +73,6 @@ Plan make_plan(const moe_config* c) {
   p.tiles = take((size_t)(p.max_tiles + 1) * 4);
   p.ntiles = take(4);
   p.sort_scratch = take(moe_k_sort_scratch_bytes(p.P, E));
-  // completion counters of the fused decode epilogues: one per sort tile
-  // (gate/up) and one per (token, 32-column block) (down)
-  p.n_counters = mx ? 0 : p.max_tiles + T * (H / 32);
-  p.counters = take((size_t)p.n_counters * 4);
   p.a = take(mx ? 0 : (size_t)p.cap * I * 4);
   p.aq = take(mx ? (size_t)p.cap * I / 2 : (size_t)p.cap * 2 * I);
   p.as = take(mx ? (size_t)p.cap * I / 32 : (size_t)p.cap * 4);
@@ -188,7 +183,7 @@ int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids, in
   if (scratch && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
   if (workspace_bytes < scratch) return MOE_ERR_WORKSPACE_TOO_SMALL;
   MOE_TRY(moe_k_sort(topk_ids, P, cfg->E, block_m, counts, offsets, sorted_pairs, pair_pos, tile_expert, n_tiles,
-                     workspace, nullptr, 0, (hipStream_t)stream));
+                     workspace, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -250,8 +245,6 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
   void* const* ev = taps ? taps->events : nullptr;
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
 
-  int32_t* counters = at<int32_t>(workspace, p.counters);
-  const int nt2 = H / 32;
 
   // route (+ for P <= 1024: top-k, sort and quantization of x in one kernel)
   MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
@@ -262,10 +255,9 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
   MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
   MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
   MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
-  // sort (also clears the fused epilogues' completion counters)
+  // sort
   MOE_TRY(mark(2 * MOE_STAGE_SORT));
-  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, counters,
-                     p.n_counters, s));
+  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
   MOE_TRY(mark(2 * MOE_STAGE_SORT + 1));
   // expert GEMMs
   if (mx) {
@@ -283,22 +275,21 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
     MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   } else {
-    // gate/up with the int8 requantization fused (last workgroup of a tile)
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
     MOE_TRY(moe_k_decode_gate_up(w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I, k,
-                                 P, a, counters, aq, (float*)as, s));
+                                 P, a, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
+    MOE_TRY(moe_k_requant_rows(a, I, sorted, offsets + E, p.cap, P, aq, (float*)as, s));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
-    // down with the combine fused (last arrival per token and column block)
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
     MOE_TRY(moe_k_decode_down(w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, H, I, k, P, y,
-                              counters + p.max_tiles, w, out, s));
+                              s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
+    MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   }
-  (void)nt2;
 
   if (taps) {
     if (taps->block_m) *taps->block_m = p.block_m;

@@ -101,26 +101,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Cross-workgroup hand-off without agent-scope fences. On gfx950 an
-// agent-scope release/acquire fence writes back / invalidates the XCD's whole
-// L2, which is ruinous when thousands of workgroups do it. Instead the data a
-// workgroup hands to another is stored and loaded with device-coherent
-// (relaxed, agent-scope) atomic accesses, which bypass the non-coherent
-// caches; a workgroup-scope release fence (wait for the stores to complete)
-// precedes the counter increment and a workgroup-scope acquire fence follows
-// the increment that hands over.
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void release_wg() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup"); }
-__device__ __forceinline__ void acquire_wg() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
-__device__ __forceinline__ int counter_add(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace moe
 
 // Scaled MFMA wrappers (gfx950). Formats: 4 = FP4 E2M1, 0 = FP8 E4M3.

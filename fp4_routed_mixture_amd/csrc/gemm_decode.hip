@@ -17,19 +17,17 @@
 // K into contiguous ranges of four-K-tile groups and reduce through LDS in a
 // fixed order. Weights stream straight from HBM into MFMA registers: the
 // prepacked layout makes each wave's load of a 32x64 tile one contiguous
-// 1 KB (16 B per lane); the next group's loads are issued before the current
-// group's MFMAs.
+// 1 KB (16 B per lane), loaded non-temporally (each weight byte is used by
+// one workgroup only).
 //
-// Fused epilogues (deterministic: every value is produced by one workgroup in
-// a fixed order; counters only decide WHICH workgroup does the final step):
-//   gate/up: a = (g * sigmoid(g)) * u in fp32 into a[pos][I]; the last of the
-//            I/32 workgroups of sort tile q (a per-tile counter) requantizes
-//            the tile's rows to int8 (s = amax/127) as FP8 hi/lo planes.
-//   down   : y[pair][H] = s_a * sum; the workgroup that completes column block
-//            j of a token (a per (token, j) counter reaching top_k) writes
-//            out[t][32j..32j+32) = fma chain over slots of w_j * y.
-// The workgroup that finishes resets its counter to 0, and the routing kernel
-// clears all counters at the start of every call.
+// Epilogues write plain fp32 results; the steps that need whole rows or all
+// of a token's pairs run as separate small kernels after the kernel boundary:
+//   gate/up: a = (g * sigmoid(g)) * u into a[pos][I]  (then requant_rows)
+//   down   : y[pair][H] = s_a * sum                    (then the combine)
+// Handing the data to another workgroup inside the kernel would need
+// device-coherent stores and a counter per tile, and every workgroup would
+// wait for its stores to complete while holding its CU: measured slower than
+// the two extra launches.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,16 +41,7 @@ __device__ __forceinline__ v16f mfma_fp4_fp8(const v4i& a, const v8i& b, v16f ac
   return MFMA_FP4_FP8(a8, b, acc, U, (int)sa, 0, (int)sb);
 }
 
-#ifndef DEC_NT
-#define DEC_NT 0       // non-temporal weight loads
-#endif
-#ifndef DEC_DB
-#define DEC_DB 0       // register double buffering of K-tile groups
-#endif
-#ifndef DEC_WAVES
-#define DEC_WAVES 4    // waves per workgroup (K split)
-#endif
-constexpr int NW = DEC_WAVES;
+constexpr int NW = 4;  // waves per workgroup (K split)
 
 template <int S>
 struct Group {
@@ -62,11 +51,7 @@ struct Group {
 };
 
 __device__ __forceinline__ v4i ld_weights(const uint8_t* p) {
-#if DEC_NT
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
-#else
-  return *reinterpret_cast<const v4i*>(p);
-#endif
 }
 
 template <int S>
@@ -123,23 +108,11 @@ __device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, 
   const uint32_t* sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (S * 256)) + lane;
   const int g0 = (G * wave) / NW, g1 = (G * (wave + 1)) / NW;
   v16f acc0 = {}, acc1 = {};
-#if DEC_DB
-  if (g0 < g1) {
-    Group<S> cur, nxt;
-    load_group<S>(cur, aptr, sptr, bptr, valid, g0, KT);
-    for (int g = g0; g < g1; ++g) {
-      if (g + 1 < g1) load_group<S>(nxt, aptr, sptr, bptr, valid, g + 1, KT);
-      mma_group<S>(cur, acc0, acc1, sb);
-      cur = nxt;
-    }
-  }
-#else
   for (int g = g0; g < g1; ++g) {
     Group<S> cur;
     load_group<S>(cur, aptr, sptr, bptr, valid, g, KT);
     mma_group<S>(cur, acc0, acc1, sb);
   }
-#endif
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     red[wave][0][v][lane] = acc0[v];
@@ -161,10 +134,8 @@ __device__ __forceinline__ float reduced(float (*red)[S][16][64], int s, int v, 
 __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ x8,
     const float* __restrict__ xs, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
-    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ a, int I,
-    int32_t* __restrict__ tile_ctr, uint8_t* __restrict__ aq8, float* __restrict__ as) {
+    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ a, int I) {
   __shared__ float red[NW][2][16][64];
-  __shared__ int last;
   const int j = blockIdx.x, q = blockIdx.y;
   if (q >= *n_tiles) return;
   const int e = tile_expert[q];
@@ -175,80 +146,27 @@ __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
   const int row = valid ? pair / top_k : 0;
   decode_mainloop<2>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
 
-  // a = (g * sigmoid(g)) * u for the hi-column lanes' rows (waves 0..3)
+  // a = (g * sigmoid(g)) * u for the hi-column lanes' rows
   const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
-  if ((l & 31) < 16 && vq < 4) {
-    const int op = q * DM + (l & 15);
-    const int opair = sorted[op];
-    if (opair < P) {
-      const float s = xs[opair / top_k];
+  if ((l & 31) >= 16) return;
+  const int op = q * DM + (l & 15);
+  const int opair = sorted[op];
+  if (opair >= P) return;
+  const float s = xs[opair / top_k];
+  float* arow = a + (size_t)op * I + j * 32;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int v = vq * 4 + vv;
-        const int n = j * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        const float gg = s * reduced<2>(red, 0, v, l), uu = s * reduced<2>(red, 1, v, l);
-        moe::st_coherent(a + (size_t)op * I + n, (gg * moe::sigmoid_fixed(gg)) * uu);
-      }
-    }
-  }
-  moe::release_wg();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = moe::counter_add(&tile_ctr[q], 1);
-    last = old == NT - 1;
-    if (last) tile_ctr[q] = 0;
-  }
-  __syncthreads();
-  if (!last) return;
-  moe::acquire_wg();
-  // requantize the tile's rows: one wave per row, loads in batches of 8
-  // values per lane (second pass re-reads from cache)
-  const int wave = threadIdx.x >> 6;
-  const int nv = I >> 6;  // values per lane, a multiple of 2
-  for (int slot = wave; slot < DM; slot += NW) {
-    const int p = q * DM + slot;
-    if (sorted[p] >= P) continue;
-    const float* arow = a + (size_t)p * I + lane;
-    uint8_t* dst = aq8 + (size_t)p * 2 * I + lane;
-    float amax = 0.f;
-#pragma unroll 1
-    for (int u0 = 0; u0 < nv; u0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = moe::ld_coherent(arow + (size_t)min(u0 + u, nv - 1) * 64);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(v[u]));  // clamped repeats do not change the max
-    }
-    amax = moe::wave_max(amax);
-    const float s = amax / 127.0f;
-    if (lane == 0) as[p] = s;
-#pragma unroll 1
-    for (int u0 = 0; u0 < nv; u0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = moe::ld_coherent(arow + (size_t)min(u0 + u, nv - 1) * 64);
-#pragma unroll 2
-      for (int u = 0; u < 8; ++u) {
-        if (u0 + u < nv) {
-          float qq = 0.f;
-          if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[u] / s), -127.f), 127.f);
-          int hi, lo;
-          moe::split_int8((int)qq, hi, lo);
-          dst[(size_t)(u0 + u) * 64] = (uint8_t)moe::small_int_to_e4m3(hi);
-          dst[I + (size_t)(u0 + u) * 64] = (uint8_t)moe::small_int_to_e4m3(lo);
-        }
-      }
-    }
+  for (int vv = 0; vv < 4; ++vv) {
+    const int v = vq * 4 + vv;
+    const float gg = s * reduced<2>(red, 0, v, l), uu = s * reduced<2>(red, 1, v, l);
+    arow[8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = (gg * moe::sigmoid_fixed(gg)) * uu;
   }
 }
 
 __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ aq8,
     const float* __restrict__ as, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
-    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ y, int H,
-    int32_t* __restrict__ tok_ctr, const float* __restrict__ w, float* __restrict__ out) {
+    const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ y, int H) {
   __shared__ float red[NW][1][16][64];
-  __shared__ int done_tok[DM];
   const int j = blockIdx.x, q = blockIdx.y;
   if (q >= *n_tiles) return;
   const int e = tile_expert[q];
@@ -259,45 +177,80 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
   decode_mainloop<1>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
 
   const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
-  if ((l & 31) < 16 && vq < 4) {
-    const int op = q * DM + (l & 15);
-    const int opair = sorted[op];
-    if (opair < P) {
-      const float s = as[op];
-      float* yrow = y + (size_t)opair * H + j * 32;
+  if ((l & 31) >= 16) return;
+  const int op = q * DM + (l & 15);
+  const int opair = sorted[op];
+  if (opair >= P) return;
+  const float s = as[op];
+  float* yrow = y + (size_t)opair * H + j * 32;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int v = vq * 4 + vv;
-        moe::st_coherent(yrow + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), s * reduced<1>(red, 0, v, l));
-      }
-    }
+  for (int vv = 0; vv < 4; ++vv) {
+    const int v = vq * 4 + vv;
+    yrow[8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = s * reduced<1>(red, 0, v, l);
   }
-  moe::release_wg();
-  __syncthreads();
-  if (threadIdx.x < DM) {
-    const int opair = sorted[q * DM + threadIdx.x];
-    int t = -1;
-    if (opair < P) {
-      const int tok = opair / top_k;
-      const int old = moe::counter_add(&tok_ctr[(size_t)tok * NT + j], 1);
-      if (old == top_k - 1) {
-        tok_ctr[(size_t)tok * NT + j] = 0;
-        t = tok;
-      }
+}
+
+// int8 requantization of the activation rows of the valid pairs: one
+// 256-thread workgroup per padded row, each thread holds I/256 values (loads
+// issued together), s = amax / 127, q = clamp(rint(a / s), +-127) stored as
+// FP8 hi/lo planes [2][I].
+__global__ __launch_bounds__(256) void requant_rows_kernel(const float* __restrict__ a, int I,
+                                                           const int32_t* __restrict__ sorted,
+                                                           const int32_t* __restrict__ n_rows, int P,
+                                                           uint8_t* __restrict__ aq8, float* __restrict__ as) {
+  __shared__ float red[4];
+  const int p = blockIdx.x, tid = threadIdx.x;
+  if (p >= *n_rows || sorted[p] >= P) return;
+  const float* arow = a + (size_t)p * I;
+  const int nu = I >> 10;  // four-element units per thread (I % 1024 == 0), else fallback below
+  float v[4][4];
+  float amax = 0.f;
+  if (nu >= 1 && nu <= 4 && (I & 1023) == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 t = *reinterpret_cast<const float4*>(arow + ((size_t)min(u, nu - 1) * 256 + tid) * 4);
+      v[u][0] = t.x; v[u][1] = t.y; v[u][2] = t.z; v[u][3] = t.w;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) amax = fmaxf(amax, fabsf(v[u][m]));
     }
-    done_tok[threadIdx.x] = t;
+  } else {
+    for (int i = tid; i < I; i += 256) amax = fmaxf(amax, fabsf(arow[i]));
   }
+  amax = moe::wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
-  moe::acquire_wg();
-  // combine the completed (token, column block) pairs: 16 slots x 32 columns
-  for (int idx = threadIdx.x; idx < DM * 32; idx += 64 * NW) {
-    const int t = done_tok[idx >> 5];
-    if (t < 0) continue;
-    const int n = j * 32 + (idx & 31);
-    float acc = 0.0f;
-    for (int jj = 0; jj < top_k; ++jj)
-      acc = __builtin_fmaf(w[(size_t)t * top_k + jj], moe::ld_coherent(y + ((size_t)t * top_k + jj) * H + n), acc);
-    out[(size_t)t * H + n] = acc;
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  if (tid == 0) as[p] = s;
+  uint8_t* dst = aq8 + (size_t)p * 2 * I;
+  auto quant1 = [&](float x) -> int {
+    float qq = 0.f;
+    if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(x / s), -127.f), 127.f);
+    return (int)qq;
+  };
+  if (nu >= 1 && nu <= 4 && (I & 1023) == 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u >= nu) break;
+      uint32_t hw = 0, lw = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        int hi, lo;
+        moe::split_int8(quant1(v[u][m]), hi, lo);
+        hw |= moe::small_int_to_e4m3(hi) << (8 * m);
+        lw |= moe::small_int_to_e4m3(lo) << (8 * m);
+      }
+      const size_t i = ((size_t)u * 256 + tid) * 4;
+      *reinterpret_cast<uint32_t*>(dst + i) = hw;
+      *reinterpret_cast<uint32_t*>(dst + I + i) = lw;
+    }
+  } else {
+    for (int i = tid; i < I; i += 256) {
+      int hi, lo;
+      moe::split_int8(quant1(arow[i]), hi, lo);
+      dst[i] = (uint8_t)moe::small_int_to_e4m3(hi);
+      dst[I + i] = (uint8_t)moe::small_int_to_e4m3(lo);
+    }
   }
 }
 
@@ -307,22 +260,27 @@ int moe_k_decode_block_m() { return DM; }
 
 hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
                                 const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
-                                int max_tiles, int H, int I, int top_k, int P, float* a, int32_t* tile_ctr,
-                                uint8_t* aq8, float* as, hipStream_t st) {
+                                int max_tiles, int H, int I, int top_k, int P, float* a, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   dim3 grid(I / 32, max_tiles);
-  decode_gate_up_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32, top_k, P, a,
-                                              I, tile_ctr, aq8, as);
+  decode_gate_up_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32, top_k, P,
+                                                  a, I);
+  return hipGetLastError();
+}
+
+hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* sorted, const int32_t* n_rows, int max_rows, int P,
+                              uint8_t* aq8, float* as, hipStream_t st) {
+  if (max_rows <= 0) return hipSuccess;
+  requant_rows_kernel<<<max_rows, 256, 0, st>>>(a, I, sorted, n_rows, P, aq8, as);
   return hipGetLastError();
 }
 
 hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
-                             int H, int I, int top_k, int P, float* y, int32_t* tok_ctr, const float* w, float* out,
-                             hipStream_t st) {
+                             int H, int I, int top_k, int P, float* y, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   dim3 grid(H / 32, max_tiles);
-  decode_down_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32, top_k, P, y, H,
-                                           tok_ctr, w, out);
+  decode_down_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32, top_k, P, y,
+                                               H);
   return hipGetLastError();
 }

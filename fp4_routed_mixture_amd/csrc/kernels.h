@@ -25,7 +25,7 @@ hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias
 size_t moe_k_sort_scratch_bytes(int P, int E);
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      int32_t* counters, int n_counters, hipStream_t st);
+                      hipStream_t st);
 
 // quant.hip
 hipError_t moe_k_quant_int8(int in_dtype, const void* v, int rows, int K, int out_fp8pair, void* q, float* scales,
@@ -41,12 +41,12 @@ hipError_t moe_k_gather_rows(const void* src, int row_bytes, const int32_t* row_
 int moe_k_decode_block_m();
 hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
                                 const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
-                                int max_tiles, int H, int I, int top_k, int P, float* a, int32_t* tile_ctr,
-                                uint8_t* aq8, float* as, hipStream_t st);
+                                int max_tiles, int H, int I, int top_k, int P, float* a, hipStream_t st);
+hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* sorted, const int32_t* n_rows, int max_rows, int P,
+                              uint8_t* aq8, float* as, hipStream_t st);
 hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
-                             int H, int I, int top_k, int P, float* y, int32_t* tok_ctr, const float* w, float* out,
-                             hipStream_t st);
+                             int H, int I, int top_k, int P, float* y, hipStream_t st);
 
 // gemm_prefill.hip
 int moe_k_prefill_block_m();

@@ -251,48 +251,36 @@ __device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K
   }
 }
 
-// k rounds of a wave argmax over s[i] = score of expert lane + 64 i, keyed
-// (score desc, expert asc). Sigmoid scores are >= 0; -1 marks experts that do
-// not exist. Lane j (< K) returns slot j: its expert in *id, its renormalized
-// weight in *w (S accumulated left to right over the slots).
-__device__ __forceinline__ void wave_select(const float (&s)[16], int K, int* id, float* w) {
-  const int lane = threadIdx.x & 63;
-  uint32_t taken = 0;
-  float my_s = 0.f;
-  int my_id = 0;
+// Rank-based top-k over the scores of one token held in LDS: the rank of
+// expert e is the number of experts that come before it in the order (score
+// desc, expert asc); the experts with rank < K are the selection and the rank
+// is the slot. No cross-lane reductions, and the same result as K rounds of
+// argmax. `stride`/`first` split the experts over the calling threads; every
+// selected expert writes its slot of sel_id / sel_s.
+__device__ __forceinline__ void rank_select(const float* __restrict__ sc, int E, int K, int first, int stride,
+                                            int* sel_id, float* sel_s) {
 #pragma unroll 1
-  for (int j = 0; j < K; ++j) {
-    float bv = -2.0f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!((taken >> i) & 1) && s[i] > bv) { bv = s[i]; bi = lane + 64 * i; }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+  for (int e = first; e < E; e += stride) {
+    const float me = sc[e];
+    int rank = 0;
+#pragma unroll 4
+    for (int f = 0; f < E; ++f) {
+      const float o = sc[f];
+      rank += (o > me) || (o == me && f < e);
     }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) { my_s = bv; my_id = bi; }
+    if (rank < K) {
+      sel_id[rank] = e;
+      sel_s[rank] = me;
+    }
   }
-  float S = 0.0f;
-#pragma unroll 1
-  for (int j = 0; j < K; ++j) S = S + __shfl(my_s, j, 64);
-  *id = my_id;
-  *w = (S == 0.0f) ? 1.0f / (float)K : my_s / S;
 }
 
-// Top-k of one token from its scores in LDS, by one wave.
-__device__ __forceinline__ void wave_topk_lds(const float* __restrict__ sc, int E, int K, int* id, float* wv) {
-  const int lane = threadIdx.x & 63;
-  float s[16];  // E <= 1024
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    s[i] = e < E ? sc[e] : -1.0f;
-  }
-  wave_select(s, K, id, wv);
+// Renormalized weights of the K selected scores: S accumulated left to right
+// over the slots, w_j = s_j / S (1/K if S == 0).
+__device__ __forceinline__ float renorm_weight(const float* sel_s, int K, int j) {
+  float S = 0.0f;
+  for (int i = 0; i < K; ++i) S = S + sel_s[i];
+  return (S == 0.0f) ? 1.0f / (float)K : sel_s[j] / S;
 }
 
 // ---------------------------------------------------------------------------
@@ -310,64 +298,64 @@ __global__ __launch_bounds__(256) void topk_quant_token_kernel(const float* __re
                                                                uint8_t* __restrict__ xs) {
   __shared__ float sc[1024];
   __shared__ float red[4];
+  __shared__ int sel_id[16];
+  __shared__ float sel_s[16];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += 256) sc[e] = moe::sigmoid_fixed(finish_logit<64>(partial, bias, T, E, t, e));
-  __syncthreads();
-  if (wave == 0) {
-    float s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = lane + 64 * i < E ? sc[lane + 64 * i] : -1.0f;
-    int id;
-    float wv;
-    wave_select(s, K, &id, &wv);
-    if (lane < K) {
-      ids_out[(size_t)t * K + lane] = id;
-      w_out[(size_t)t * K + lane] = wv;
-    }
-  }
-  if (!quant) return;
   const XT* row = x + (size_t)t * H;
-  if (mx) {
-    if (wave == 1) wave_quant_row<XT>(row, H, 1, xq + (size_t)t * (H / 2), xs + (size_t)t * (H / 32));
-    return;
-  }
-  // int8 row: every thread holds H/256 values (H % 256 == 0), loads issued together
-  const int nu = H >> 10;  // four-element units per thread
-  float amax = 0.f;
-  for (int u0 = 0; u0 < nu; u0 += 4) {
-    float v[4][4];
+  // int8 rows of up to 4096 values: each thread's 16 values are loaded first,
+  // so the row and the chunk sums are in flight together
+  const bool regs = quant && !mx && H <= 4096 && (H & 1023) == 0;
+  const int nu = H >> 10;
+  float v[4][4];
+  if (regs) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u0 + u, nu - 1) * 256 + tid) * 4, v[u]);
+    for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u, nu - 1) * 256 + tid) * 4, v[u]);
+  }
+#pragma unroll 1
+  for (int e = tid; e < E; e += 256) sc[e] = moe::sigmoid_fixed(finish_logit<64>(partial, bias, T, E, t, e));
+  float amax = 0.f;
+  if (regs) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) amax = fmaxf(amax, fabsf(v[u][m]));
+    amax = moe::wave_max(amax);
+    if (lane == 0) red[wave] = amax;
   }
-  // H not a multiple of 1024: the remaining 256-element units
-  for (int i = nu * 1024 + tid * 4; i < H; i += 1024) {
-    float v[4];
-    load4<XT>(row + i, v);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-  }
-  amax = moe::wave_max(amax);
-  if (lane == 0) red[wave] = amax;
   __syncthreads();
+  rank_select(sc, E, K, tid, 256, sel_id, sel_s);
+  __syncthreads();
+  if (tid < K) {
+    ids_out[(size_t)t * K + tid] = sel_id[tid];
+    w_out[(size_t)t * K + tid] = renorm_weight(sel_s, K, tid);
+  }
+  if (!quant) return;
+  if (!regs) {
+    if (wave == 1) {
+      const size_t qrow = mx ? (size_t)H / 2 : (size_t)2 * H;
+      const size_t srow = mx ? (size_t)H / 32 : 4;
+      wave_quant_row<XT>(row, H, mx, xq + t * qrow, xs + t * srow);
+    }
+    return;
+  }
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax / 127.0f;
   if (tid == 0) reinterpret_cast<float*>(xs)[t] = s;
   uint8_t* q = xq + (size_t)t * 2 * H;
-  for (int i = tid * 4; i < H; i += 1024) {
-    float v[4];
-    load4<XT>(row + i, v);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u >= nu) break;
     uint32_t hw = 0, lw = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float qq = 0.f;
-      if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
+      if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[u][m] / s), -127.f), 127.f);
       int hi, lo;
       moe::split_int8((int)qq, hi, lo);
       hw |= moe::small_int_to_e4m3(hi) << (8 * m);
       lw |= moe::small_int_to_e4m3(lo) << (8 * m);
     }
+    const size_t i = ((size_t)u * 256 + tid) * 4;
     *reinterpret_cast<uint32_t*>(q + i) = hw;
     *reinterpret_cast<uint32_t*>(q + H + i) = lw;
   }
@@ -383,17 +371,24 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
                                                          int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                                                          uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
   __shared__ float sc[4][1024];
+  __shared__ int sel_id[4][16];
+  __shared__ float sel_s[4][16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
 #pragma unroll 1
   for (int e = lane; e < E; e += 64) sc[wave][e] = moe::sigmoid_fixed(finish_logit<8>(partial, bias, T, E, t, e));
-  int id;
-  float wv;
-  wave_topk_lds(sc[wave], E, K, &id, &wv);
+  // a wave reads only its own LDS rows: wave-level ordering suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  rank_select(sc[wave], E, K, lane, 64, sel_id[wave], sel_s[wave]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < K) {
-    ids_out[(size_t)t * K + lane] = id;
-    w_out[(size_t)t * K + lane] = wv;
+    ids_out[(size_t)t * K + lane] = sel_id[wave][lane];
+    w_out[(size_t)t * K + lane] = renorm_weight(sel_s[wave], K, lane);
   }
   if (quant) {
     const size_t qrow = mx ? (size_t)H / 2 : (size_t)2 * H;

@@ -26,10 +26,8 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
                                                           int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ n_tiles,
-                                                          int32_t* __restrict__ counters, int n_counters) {
+                                                          int32_t* __restrict__ n_tiles) {
   extern __shared__ int smem[];
-  for (int i = threadIdx.x; i < n_counters; i += 1024) counters[i] = 0;
   int* wcnt = smem;                  // 17 * E
   int* offs = wcnt + 17 * E;         // E + 1
   int* tmp = offs + E + 1;           // 1024
@@ -71,10 +69,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted,
                                                          int32_t* __restrict__ tile_expert,
-                                                         int32_t* __restrict__ n_tiles,
-                                                         int32_t* __restrict__ counters, int n_counters) {
+                                                         int32_t* __restrict__ n_tiles) {
   extern __shared__ int smem[];
-  for (int i = threadIdx.x; i < n_counters; i += 1024) counters[i] = 0;
   int* tot = smem;            // E
   int* offs = tot + E;        // E + 1
   int* tmp = offs + E + 1;    // 1024
@@ -121,7 +117,7 @@ size_t moe_k_sort_scratch_bytes(int P, int E) {
 
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      int32_t* counters, int n_counters, hipStream_t st) {
+                      hipStream_t st) {
   // gfx950 has 160 KB of LDS per workgroup; above 64 KB a kernel must opt in
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
@@ -135,8 +131,7 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
   }
   if (P <= moe::SB) {
     size_t lds = (size_t)(17 * E + E + 1 + 1024) * 4;
-    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles,
-                                            counters, n_counters);
+    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles);
     return hipGetLastError();
   }
   int nb = (P + moe::SB - 1) / moe::SB;
@@ -146,8 +141,7 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, 1024, (size_t)(E + E + 1 + 1024) * 4, st>>>(nb, P, E, block_m, block_hist, counts, offsets,
-                                                                    sorted, tile_expert, n_tiles, counters,
-                                                                    n_counters);
+                                                                    sorted, tile_expert, n_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scatter_kernel<<<(P + 255) / 256, 256, 0, st>>>(ids, P, E, local_rank, block_hist, sorted, pos);
