@@ -6,18 +6,20 @@
 // MXFP4 (E2M1 codes + E8M0 per 32) and go to V_MFMA_SCALE_F32_32X32X64_F8F6F4
 // unchanged: weights are A (32-row tiles), pair rows are B (32 columns).
 //
-// Workgroup tile: BM = 64 pair rows (one sort tile of one expert, two 32-row
-// pair tiles) x 4 waves, each wave owning 4 weight tiles of 32 rows (2
-// gate/up tile pairs of W13, or 4 row tiles of W2): 8 accumulators, half the
-// accumulation register file, so that two workgroups share a CU and one's
+// Workgroup tile: BM = 32 NU pair rows (one sort tile of one expert) x 4
+// waves, each wave owning 8/NU weight tiles of 32 rows (gate/up tile pairs
+// of W13, or row tiles of W2) against all NU pair tiles: 8 accumulators, half
+// the accumulation register file, so that two workgroups share a CU and one's
 // prologue and epilogue (SiLU, requantization, stores) run under the other's
-// MFMAs. Weight tiles are used by one wave only, so they go from HBM straight
-// into the MFMA operand registers: the prepacked layout stores each 64-K step
-// of a tile as 64 lanes x 16 bytes, one fully coalesced load per tile and
-// K-step, kept PF K-steps ahead in a register ring. The gathered pair rows
-// are shared by the 4 waves and go through LDS: each stage (128 K) is loaded
-// into registers two stages ahead, transposed into the operand layout on its
-// LDS store, and double-buffered.
+// MFMAs. NU = 2 (64-row sort tiles, 4 weight tiles per wave) measures faster
+// than NU = 4 on the Zipf prefill workloads and wastes less padding on small
+// experts. Weight tiles are used by one wave only, so they go from HBM
+// straight into the MFMA operand registers: the prepacked layout stores each
+// 64-K step of a tile as 64 lanes x 16 bytes, one fully coalesced load per
+// tile and K-step, kept PF K-steps ahead in a register ring. The gathered pair
+// rows are shared by the 4 waves and go through LDS: each stage (128 K) is
+// loaded into registers two stages ahead, transposed into the operand layout
+// on its LDS store, and double-buffered.
 //
 // Scale dwords (four K-steps each) are loaded one group ahead; the MFMA's
 // byte select picks the K-step. The main loop has no branch between a load
@@ -37,17 +39,21 @@
 
 namespace {
 
-constexpr int NU = 2;            // 32-row pair tiles per sort tile
-constexpr int BM = 32 * NU;      // pair rows per sort tile
-constexpr int WTW = 4;           // 32-row weight tiles per wave
+#ifndef MOE_PREFILL_NU
+#define MOE_PREFILL_NU 2
+#endif
+constexpr int NU = MOE_PREFILL_NU;       // 32-row pair tiles per sort tile (2 or 4)
+constexpr int BM = 32 * NU;              // pair rows per sort tile
+constexpr int WTW = 8 / NU;              // 32-row weight tiles per wave (4 or 2)
 constexpr int NWAVE = 4;
 #ifndef MOE_PREFILL_PF
 #define MOE_PREFILL_PF 4
 #endif
 constexpr int PF = MOE_PREFILL_PF;       // weight prefetch depth in 64-K steps (2 or 4)
 constexpr int B_STAGE = NU * 2 * 1024;   // BM pair rows x 128 K, operand layout
+constexpr int NBL = BM * 4 / (NWAVE * 64);  // 16-byte pair-row loads per thread and stage
 static_assert(PF == 2 || PF == 4, "ring slots are K-step % PF within a 4-step scale group");
-static_assert(BM * 4 == NWAVE * 64, "one 16-byte pair-row load per thread and stage");
+static_assert(NBL >= 1 && WTW % 2 == 0, "whole pair-row loads, whole gate/up pairs");
 
 template <int OA, int OB>
 __device__ __forceinline__ v16f mfma44(const v4i& a, const v4i& b, v16f acc, uint32_t sa, uint32_t sb) {
@@ -93,15 +99,17 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   };
   const uint32_t* sa_base = reinterpret_cast<const uint32_t*>(wsc + ((size_t)e * NT + ubase) * G * (S * 256)) + lane;
 
-  // ---- gathered pair rows: one load of BM rows x 64 bytes per stage ----------
-  // thread -> row tid/4, 16-byte chunk tid%4 of the stage's 64 bytes
-  const int br = tid >> 2, c4 = tid & 3;
-  const int b_dst = ((br >> 5) * 2 + (c4 >> 1)) * 1024 + ((c4 & 1) * 32 + (br & 31)) * 16;
-  uint32_t b_off;
-  {
+  // ---- gathered pair rows: NBL loads of 64 rows x 64 bytes per stage -------
+  // load m: thread -> row 64m + tid/4, 16-byte chunk tid%4 of the stage's 64 bytes
+  const int c4 = tid & 3;
+  const int b_dst = (((tid >> 2) >> 5) * 2 + (c4 >> 1)) * 1024 + ((c4 & 1) * 32 + ((tid >> 2) & 31)) * 16;
+  uint32_t b_off[NBL];
+#pragma unroll
+  for (int m = 0; m < NBL; ++m) {
+    const int br = m * 64 + (tid >> 2);
     const int pr = sorted[q * BM + br];
     const int row = pr < P ? (rows_are_tokens ? pr / top_k : q * BM + br) : 0;  // padding reads row 0
-    b_off = (uint32_t)row * (uint32_t)(K >> 1) + c4 * 16;
+    b_off[m] = (uint32_t)row * (uint32_t)(K >> 1) + c4 * 16;
   }
   // scale-row offsets of this lane's pair rows (one per pair tile)
   uint32_t sb_off[NU];
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     for (int u = 0; u < NU; ++u) acc[t][u] = (v16f){};
 
   v4i ra[PF][WTW];      // weight ring: slot kt % PF
-  v4i rb[2];            // pair-row staging, set = stage & 1
+  v4i rb[2][NBL];       // pair-row staging, set = stage & 1
   uint32_t sa[WTW], sx[NU], sy[NU], na[WTW], nx[NU], ny[NU];
 
   auto aload = [&](int slot, int kt) {
@@ -130,9 +138,13 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   };
   auto bload = [&](int set, int st) {
     st = st < NS ? st : NS - 1;
-    rb[set] = *reinterpret_cast<const v4i*>(act_codes + b_off + (uint32_t)st * 64);
+#pragma unroll
+    for (int m = 0; m < NBL; ++m) rb[set][m] = *reinterpret_cast<const v4i*>(act_codes + b_off[m] + (uint32_t)st * 64);
   };
-  auto bstore = [&](int set, int buf) { *reinterpret_cast<v4i*>(&lds_b[buf][b_dst]) = rb[set]; };
+  auto bstore = [&](int set, int buf) {
+#pragma unroll
+    for (int m = 0; m < NBL; ++m) *reinterpret_cast<v4i*>(&lds_b[buf][b_dst + m * 4096]) = rb[set][m];
+  };
   auto load_scales = [&](uint32_t* da, uint32_t* dx, uint32_t* dy, int g) {
     g = g < G ? g : G - 1;
 #pragma unroll
