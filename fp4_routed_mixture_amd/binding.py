@@ -25,7 +25,8 @@ STAGES = ["router", "topk", "quant_x", "sort", "gate_up", "requant", "down", "co
 # every function that include/fp4moe.h declares
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_workspace_size",
            "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_sort", "moe_quantize",
-           "moe_forward", "moe_forward_taps", "moe_rmsnorm", "moe_residual_add"]
+           "moe_forward", "moe_forward_taps", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_size",
+           "moe_forward_stack"]
 
 
 class MoEError(RuntimeError):
@@ -80,6 +81,8 @@ def lib():
                                            C.POINTER(moe_taps), vp, sz, vp]),
             "moe_rmsnorm": (C.c_int, [i32, i32, vp, vp, vp]),
             "moe_residual_add": (C.c_int, [i64, vp, vp, vp]),
+            "moe_stack_workspace_size": (C.c_int, [cfgp, C.POINTER(sz)]),
+            "moe_forward_stack": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -198,3 +201,20 @@ def moe_rmsnorm(T, H, x, out, stream=None):
 
 def moe_residual_add(n, x, y, stream=None):
     _check(lib().moe_residual_add(n, _p(x), _p(y), _s(stream)), "moe_residual_add")
+
+
+def moe_stack_workspace_size(cfg) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_stack_workspace_size(C.byref(cfg), C.byref(n)), "moe_stack_workspace_size")
+    return n.value
+
+
+def moe_forward_stack(cfg, x, layers, workspace, layer_out=None, stream=None):
+    """layers: sequence of dicts with router_w, bias (or None), w13, w13s, w2,
+    w2s device tensors (prepacked weights). x (fp32 [T][H]) is updated in
+    place; layer_out (fp32 [L][T][H] or None) receives each layer's output."""
+    L = len(layers)
+    arr = lambda key: (C.c_void_p * max(L, 1))(*[_p(d[key]) for d in layers])
+    keep = [arr(k) for k in ("router_w", "bias", "w13", "w13s", "w2", "w2s")]
+    _check(lib().moe_forward_stack(C.byref(cfg), L, _p(x), *[C.cast(a, C.c_void_p) for a in keep], _p(layer_out),
+                                   _p(workspace), workspace.numel(), _s(stream)), "moe_forward_stack")

@@ -326,6 +326,45 @@ int moe_forward(const moe_config* cfg, const void* x, const float* router_w, con
                           nullptr, workspace, workspace_bytes, stream);
 }
 
+int moe_stack_workspace_size(const moe_config* cfg, size_t* bytes) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = make_plan(cfg).total + 2 * up256((size_t)cfg->T * cfg->H * 4);
+  return MOE_OK;
+}
+int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* const* router_w,
+                      const float* const* router_bias, const uint8_t* const* w13, const uint8_t* const* w13_scale,
+                      const uint8_t* const* w2, const uint8_t* const* w2_scale, float* layer_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (cfg->x_dtype != MOE_X_F32) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (L < 0) return MOE_ERR_INVALID_ARG;
+  if (L == 0 || cfg->T == 0) return MOE_OK;
+  if (!x || !router_w || !w13 || !w13_scale || !w2 || !w2_scale || !workspace) return MOE_ERR_INVALID_ARG;
+  const size_t fw = make_plan(cfg).total, nb = (size_t)cfg->T * cfg->H * 4;
+  const size_t need = fw + 2 * up256(nb);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(x) || (layer_out && !aligned16(layer_out)) || ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  if (overlaps(workspace, need, x, nb) || (layer_out && overlaps(workspace, need, layer_out, nb * L)) ||
+      (layer_out && overlaps(x, nb, layer_out, nb * L)))
+    return MOE_ERR_ALIAS;
+  for (int l = 0; l < L; ++l)
+    if (!router_w[l] || !w13[l] || !w13_scale[l] || !w2[l] || !w2_scale[l]) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  float* xn = at<float>(workspace, fw);
+  float* ybuf = at<float>(workspace, fw + up256(nb));
+  for (int l = 0; l < L; ++l) {
+    float* yl = layer_out ? layer_out + (size_t)l * cfg->T * cfg->H : ybuf;
+    MOE_TRY(moe_k_rmsnorm(x, cfg->T, cfg->H, xn, s));
+    st = moe_forward_taps(cfg, xn, router_w[l], router_bias ? router_bias[l] : nullptr, w13[l], w13_scale[l], w2[l],
+                          w2_scale[l], yl, nullptr, nullptr, nullptr, workspace, fw, stream);
+    if (st) return st;
+    MOE_TRY(moe_k_residual(x, yl, (int64_t)cfg->T * cfg->H, s));
+  }
+  return MOE_OK;
+}
 int moe_rmsnorm(int32_t T, int32_t H, const float* x, float* out, void* stream) {
   if (T < 0 || H < 64 || H % 64 || H > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return MOE_OK;

@@ -251,6 +251,27 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
 int moe_rmsnorm(int32_t T, int32_t H, const float* x, float* out, void* stream);
 int moe_residual_add(int64_t n, float* x, const float* y, void* stream);
 
+/* ----------------------------------------------------------- layer stack --
+ * A stack of MoE layers with the residual update between them, as in the
+ * 43-layer routed stack of the serving system the pages describe ("DeepSeek
+ * V4 Flash on 8x AMD gfx1201", model description: 43 layers of 256 routed
+ * experts, 6 active per token). For l = 0 .. L-1:
+ *     x <- x + moe_l(rmsnorm(x))
+ * with x fp32 [T][H] updated in place (cfg->x_dtype must be MOE_X_F32; the
+ * layer's input is the normalized stream, fp32). Per-layer device pointers
+ * come in HOST arrays of length L: router_w[l], w13[l], w13_scale[l], w2[l],
+ * w2_scale[l] (prepacked), router_bias[l] (router_bias itself or any entry
+ * may be NULL). layer_out (device fp32 [L][T][H], nullable) receives every
+ * layer's moe output, for teacher-forced checks of one layer at a time.
+ * workspace: at least moe_stack_workspace_size bytes, 256-byte aligned, not
+ * overlapping x or layer_out. Returns the first failing layer's status;
+ * layers before it have been applied to x. */
+int moe_stack_workspace_size(const moe_config* cfg, size_t* bytes);
+int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* const* router_w,
+                      const float* const* router_bias, const uint8_t* const* w13, const uint8_t* const* w13_scale,
+                      const uint8_t* const* w2, const uint8_t* const* w2_scale, float* layer_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

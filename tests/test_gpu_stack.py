@@ -1,0 +1,62 @@
+"""The 43-layer decode stack (x <- x + moe_l(rmsnorm(x)), 43 layers with
+distinct weights, 32 tokens, int8 activations) through moe_forward_stack,
+checked teacher-forced: the input of a sampled layer is rebuilt on the host
+from the starting stream and the per-layer outputs the call returns (the
+residual update is one fp32 add, reproduced exactly), normalized by the
+oracle's RMSNorm and run through the oracle's layer, which must match the
+device's output for that layer bit for bit (every step is exact in int8
+mode)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_routed_mixture_amd import binding as B
+from fp4_routed_mixture_amd import synth as S
+from fp4_routed_mixture_amd import synth_device as SD
+from gpu_util import oracle_layer, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _run_stack(w, L):
+    layers = []
+    for l in range(L):
+        layers.append(SD.load_layer(w, l))
+    torch.cuda.synchronize()
+    cfg = SD.config(w)
+    ws = torch.empty(B.moe_stack_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    x0 = S.activations(w)  # fp32 [T][H]
+    x = torch.from_numpy(x0).cuda()
+    y = torch.empty((L, w.T, w.H), dtype=torch.float32, device="cuda")
+    B.moe_forward_stack(cfg, x, layers, ws, layer_out=y)
+    torch.cuda.synchronize()
+    out = x.cpu().numpy(), y.cpu().numpy()
+    del layers, ws, x, y
+    torch.cuda.empty_cache()
+    return x0, out[0], out[1]
+
+
+@pytest.mark.parametrize("name,L,check", [("stack43_decode_t32", 43, (0, 1, 21, 42))])
+def test_stack_teacher_forced(name, L, check):
+    w = S.WORKLOADS[name]
+    print(f"[stack] {S.describe(w)} layers={L}", flush=True)
+    x0, xL, y = _run_stack(w, L)
+    assert np.isfinite(y).all() and np.isfinite(xL).all()
+    # the residual stream, rebuilt on the host
+    xs = [x0]
+    for l in range(L):
+        xs.append((xs[-1] + y[l]).astype(np.float32))
+    assert np.array_equal(xs[L], xL)
+    for l in check:
+        print(f"[stack] layer {l}", flush=True)
+        xn = oracle.rmsnorm(xs[l])
+        o = oracle_layer(w, xn, layer=l)
+        assert np.array_equal(o["out"], y[l]), f"layer {l}: max |diff| {np.abs(o['out'] - y[l]).max()}"
