@@ -170,6 +170,59 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
     }
 
 
+def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: float = 20.0) -> dict:
+    """The layer stack (x <- x + moe_l(rmsnorm(x)) over all layers, distinct
+    weights per layer, all resident) through moe_forward_stack. A step is one
+    pass over every layer for one decode batch."""
+    w = S.WORKLOADS[name]
+    L, T = w.layers, w.T
+    layers = [SD.load_layer(w, layer=l) for l in range(L)]
+    cfg = SD.config(w)
+    ws = torch.empty(B.moe_stack_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    x0 = torch.from_numpy(S.activations(w)).cuda()
+    x = x0.clone()
+    for _ in range(warmup):
+        B.moe_forward_stack(cfg, x, layers, ws)
+    torch.cuda.synchronize()
+    x.copy_(x0)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(sleep_ms * 2.4e6))
+    t_start.record()
+    h0 = time.perf_counter()
+    for _ in range(steps):
+        B.moe_forward_stack(cfg, x, layers, ws)
+    host_s = time.perf_counter() - h0
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+
+    # routing of every layer on the first step's stream (diagnostic, untimed):
+    # the distinct experts each layer reads set the algorithmic bytes
+    x.copy_(x0)
+    y = torch.empty((L, T, w.H), dtype=torch.float32, device="cuda")
+    B.moe_forward_stack(cfg, x, layers, ws, layer_out=y)
+    xl = x0.clone()
+    rcfg = SD.config(w)
+    rws = SD.workspace(rcfg)
+    xn = torch.empty_like(xl)
+    ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    distinct = []
+    for l in range(L):
+        B.moe_rmsnorm(T, w.H, xl, xn)
+        B.moe_route(rcfg, xn, layers[l]["router_w"], layers[l]["bias"], ids, wts, rws)
+        distinct.append(len(np.unique(ids.cpu().numpy())))
+        xl += y[l]
+    b13, b2 = per_expert_bytes(w)
+    step_bytes = sum(d * (b13 + b2) + w.E * w.H * 4 + 2 * T * w.H * 4 for d in distinct)
+    del layers
+    return {"workload": name, "layers": L, "T": T, "steps": steps, "ms_per_step": ms_step,
+            "tokens_per_s": T / (ms_step / 1e3), "host_enqueue_ms": host_s * 1e3 / steps,
+            "gpu_bound": host_s < sleep_ms / 1e3 + steps * ms_step / 1e3,
+            "distinct_experts_per_layer": float(np.mean(distinct)), "step_alg_bytes": step_bytes,
+            "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9}
+
+
 def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
     """The oracle, untuned, on the host cores: whole layers of the same
     workload (rotating the same seeded batches) until about budget_s of CPU
@@ -226,6 +279,8 @@ def main():
     ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
     ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is not sharded here",
@@ -236,6 +291,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (no HIP device visible)", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel(), "launches": 3}))
+        return
     from fp4_routed_mixture_amd import binding as B
     from fp4_routed_mixture_amd import synth as S
     from fp4_routed_mixture_amd import synth_device as SD
@@ -248,13 +311,18 @@ def main():
           file=sys.stderr, flush=True)
     legs = {}
     if not args.no_legs:
-        for name, steps, rot in (("decode_t64_zipf", 32, 8), ("prefill_t4604_zipf", 10, 2)):
+        for name, steps, rot in (("decode_t64_zipf", 32, 8), ("prefill_t4604_zipf", 10, 2),
+                                 ("prefill_t16384_zipf", 4, 2)):
             torch.cuda.empty_cache()
             r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev)
             legs[name] = r
             print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tokens_per_s']:.0f} tok/s, "
                   f"layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
                   + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        stack = run_stack("stack43_decode_t32", 5, 1, torch, B, S, SD)
+        print(f"# stack43_decode_t32: {stack['ms_per_step']:.2f} ms/step (43 layers), {stack['tokens_per_s']:.0f} "
+              f"tok/s, {stack['hbm_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     w = S.WORKLOADS[args.workload]
     mx = w.act_mode == S.ACT_MXFP4
@@ -300,6 +368,13 @@ def main():
                      "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
                      "distinct_experts": v["distinct_experts"]} for k, v in legs.items()},
     }
+    if not args.no_legs:
+        line["legs"]["stack43_decode_t32"] = {
+            "tokens_per_s": round(stack["tokens_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
+            "layers": stack["layers"], "hbm_gbs": round(stack["hbm_gbs"], 1),
+            "hbm_frac": round(stack["hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "distinct_experts_per_layer": stack["distinct_experts_per_layer"],
+            "host_enqueue_ms_per_step": round(stack["host_enqueue_ms"], 3)}
     print(json.dumps(line))
 
 
