@@ -1,9 +1,8 @@
 // Low-M (decode) expert GEMMs: packed E2M1 weights x int8 activations.
 //
-// The pages' CDNA2 decode kernel used dot-product instructions on int8
-// activations ("INT8 activation quantization", "CDNA2 dot-product
-// instructions", abstract of "DeepSeek-V4-Flash on AMD gfx90a: Correctness
-// Recovery and Inference Performance Engineering"); on gfx950 the FP4
+// The CDNA2 decode kernel of DeepSeek-V4-Flash on AMD gfx90a: Correctness
+// Recovery and Inference Performance Engineering (abstract) multiplies int8
+// activations with dot-product instructions; on gfx950 the FP4
 // operand goes to the scaled MFMA unchanged, so there is no format mismatch:
 // each int8 activation q is given to the FP4 x FP8 scaled MFMA as the exact
 // pair q = 16*hi + lo (hi, lo small integers in E4M3), the hi columns carrying

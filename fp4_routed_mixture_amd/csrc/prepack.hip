@@ -1,7 +1,7 @@
 // Load-time relayout of packed FP4 expert weights into the operand order of
-// the gfx950 32x32x64 scaled MFMA ("repair the weight layout at load time",
-// abstract of "DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and
-// Inference Performance Engineering").
+// the gfx950 32x32x64 scaled MFMA; it also carries the load-time layout
+// repair of DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and
+// Inference Performance Engineering (abstract).
 //
 // Canonical layout: codes [E][N][K/2] (low nibble = even k), E8M0 scales
 // [E][N][K/32].

@@ -1,6 +1,6 @@
-// Activation quantization ("INT8 activation quantization", abstract of
-// "DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and Inference
-// Performance Engineering"; MXFP4 per the OCP Microscaling v1.0 rules).
+// Activation quantization (int8 rows as in the decode path of DeepSeek-V4-
+// Flash on AMD gfx90a: Correctness Recovery and Inference Performance
+// Engineering, abstract; MXFP4 per the OCP Microscaling v1.0 rules).
 //
 // int8 rows: s = amax / 127, q = clamp(rint(v / s), -127, 127); amax = 0 gives
 // s = 0, q = 0. Besides plain int8 output, the forward path stores each q as

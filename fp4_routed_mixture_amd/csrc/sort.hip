@@ -1,5 +1,5 @@
-// Expert sort ("retuned expert sorting", abstract of "DeepSeek-V4-Flash on
-// AMD gfx90a: Correctness Recovery and Inference Performance Engineering"):
+// Expert sort (retuned for prefill in DeepSeek-V4-Flash on AMD gfx90a:
+// Correctness Recovery and Inference Performance Engineering, abstract):
 // a stable counting sort of the P = T*k (token, slot) pairs by expert, each
 // expert segment padded to a multiple of block_m, plus the tile -> expert map
 // the grouped GEMMs walk. Integers only, so it is bit-exact by construction.

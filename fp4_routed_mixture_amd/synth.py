@@ -5,9 +5,10 @@ routing, no quantization, no GEMM): both the HIP path and the CPU oracle take
 their inputs from here, so it must stay free of either side's code.
 
 Workloads (shapes from the DeepSeek-V4-Flash pages: 256 routed experts, 6 per
-token and 43 layers on the gfx1201 deployment blog, "What we set out to do";
-the 4,604-token prompt in the MI250 paper's abstract; hidden 4096 and expert
-intermediate 2048 from the problem statement):
+token and 43 layers on the gfx1201 deployment blog, section What we set out to
+do; the 4,604-token prompt in the MI250 paper's abstract; hidden 4096 and
+expert intermediate 2048, which with 43 x 256 x 3 matrices give the 277B
+routed parameters of the blog's 284B-parameter model):
 
   tiny              T=4,     H=256,  I=128,  E=8,   k=2, fp32 x, uniform router
   decode_t4         T=4,     H=4096, I=2048, E=256, k=6, bf16 x, uniform, int8

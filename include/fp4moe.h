@@ -2,13 +2,14 @@
  * fp4moe.h -- C ABI of the routed mixture-of-experts layer with packed FP4
  * experts, written for AMD Instinct MI355X (gfx950, CDNA4).
  *
- * The layer is the "FP4 routed mixture-of-experts computation" of the
- * DeepSeek-V4-Flash paper ("DeepSeek-V4-Flash on AMD gfx90a: Correctness
- * Recovery and Inference Performance Engineering", abstract): packed FP4
- * expert weights, INT8 activation quantization for decode, expert sorting,
- * and a load-time repair of the weight layout. The model facts (256 routed
- * experts, 6 active per token) are those of "DeepSeek V4 Flash on 8x AMD
- * gfx1201: packaged TP=8 deployment", section "What we set out to do".
+ * The layer is the routed mixture of experts with FP4 expert weights that
+ * the DeepSeek-V4-Flash paper runs on MI250 (DeepSeek-V4-Flash on AMD gfx90a:
+ * Correctness Recovery and Inference Performance Engineering, abstract): FP4
+ * packed expert weights, int8-quantized activations for decode, a sort of the
+ * tokens by expert, and a repair of the weight layout when the weights are
+ * loaded. The model facts (256 routed experts, 6 active per token, 43 layers)
+ * come from DeepSeek V4 Flash on 8x AMD gfx1201: packaged TP=8 deployment,
+ * section What we set out to do.
  *
  * For one batch of T tokens it computes
  *   l[t,e]   = <x[t,:], Wr[e,:]> (+ b[e])               fp32, fixed order
@@ -156,8 +157,8 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* ---------------------------------------------------------------- weights --
  * Expert weights are packed E2M1 codes with one E8M0 scale per 32 elements
- * along K ("packed FP4 weights", abstract of the gfx90a paper; element and
- * scale formats from OCP Microscaling v1.0).
+ * along K (the FP4 expert weights of the gfx90a paper's abstract; element
+ * and scale formats from OCP Microscaling v1.0).
  * Canonical layout (the interchange format):
  *   W13 (which = MOE_W13, N = 2I rows, K = H): codes [E][2I][H/2], scales
  *       [E][2I][H/32]; rows 0..I-1 are the gate projection, I..2I-1 the up
@@ -170,7 +171,7 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
  * gate and up tiles interleaved, scales grouped four K-tiles to a dword. The
  * packing is a bijection; moe_unpack inverts it.
  *
- * "Repair the weight layout at load time" (abstract of the gfx90a paper):
+ * The load-time layout repair of the gfx90a paper (abstract) is
  * row_perm (device int32 [N], or NULL for the identity) makes packed row r
  * hold canonical row row_perm[r] of every expert, codes and scales together.
  * A matrix whose rows were stored in the permuted order pi is repaired by
@@ -195,7 +196,7 @@ int moe_route(const moe_config* cfg, const void* x, const float* router_w, const
               int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ sort --
- * "Retuned expert sorting" (abstract of the gfx90a paper): group the P pairs
+ * Expert sort (the gfx90a paper retunes it for prefill, abstract): group the P pairs
  * (p = t * top_k + j) by expert, keeping ascending p within an expert, each
  * expert's segment padded up to a multiple of block_m (1 <= block_m <= 1024).
  *   counts [E]          pairs per expert
@@ -213,8 +214,8 @@ int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids,
 
 /* -------------------------------------------------------------- quantize --
  * Quantize rows of an activation matrix v [rows][K] (in_dtype: MOE_X_F32 or
- * MOE_X_BF16) with cfg->act_mode ("INT8 activation quantization", abstract of
- * the gfx90a paper; MXFP4 per OCP Microscaling v1.0).
+ * MOE_X_BF16) with cfg->act_mode (int8 rows as the gfx90a paper quantizes
+ * decode activations, abstract; MXFP4 per OCP Microscaling v1.0).
  *   INT8 : q int8 [rows][K], scales fp32 [rows]. K % 64 == 0.
  *   MXFP4: q codes [rows][K/2], scales E8M0 [rows][K/32]. K % 64 == 0. */
 int moe_quantize(const moe_config* cfg, int32_t rows, int32_t K, int32_t in_dtype,
@@ -253,8 +254,8 @@ int moe_residual_add(int64_t n, float* x, const float* y, void* stream);
 
 /* ----------------------------------------------------------- layer stack --
  * A stack of MoE layers with the residual update between them, as in the
- * 43-layer routed stack of the serving system the pages describe ("DeepSeek
- * V4 Flash on 8x AMD gfx1201", model description: 43 layers of 256 routed
+ * 43-layer routed stack of the model (DeepSeek V4 Flash on 8x AMD gfx1201:
+ * packaged TP=8 deployment, What we set out to do: 43 layers of 256 routed
  * experts, 6 active per token). For l = 0 .. L-1:
  *     x <- x + moe_l(rmsnorm(x))
  * with x fp32 [T][H] updated in place (cfg->x_dtype must be MOE_X_F32; the

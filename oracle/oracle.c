@@ -7,12 +7,11 @@
  * with the HIP library; both sides take their inputs from the seeded generators
  * and nothing else.
  *
- * What it computes (the layer the pages centre on: "FP4 routed
- * mixture-of-experts computation" with "packed FP4 weights" and "INT8
- * activation quantization", abstract of "DeepSeek-V4-Flash on AMD gfx90a:
- * Correctness Recovery and Inference Performance Engineering"; 256 routed
- * experts with 6 active per token, "What we set out to do" in "DeepSeek V4
- * Flash on 8x AMD gfx1201: packaged TP=8 deployment"):
+ * What it computes (the routed mixture of experts with FP4 packed expert
+ * weights and int8-quantized decode activations of DeepSeek-V4-Flash on AMD
+ * gfx90a: Correctness Recovery and Inference Performance Engineering,
+ * abstract; 256 routed experts with 6 active per token from DeepSeek V4
+ * Flash on 8x AMD gfx1201: packaged TP=8 deployment, What we set out to do):
  *
  *   1. router logits  l[t,e] = <x[t,:], Wr[e,:]> (+ b[e])            fp32
  *   2. scores s = sigmoid(l); the k largest (ties -> lower expert);
@@ -192,7 +191,7 @@ void or_topk(int T, int E, int k, const float* logits, int32_t* ids, float* w, f
 }
 
 /* ------------------------------------------------------------------------ */
-/* Expert sort ("retuned expert sorting", abstract of the gfx90a paper)     */
+/* Expert sort (retuned for prefill in the gfx90a paper, abstract)         */
 /* ------------------------------------------------------------------------ */
 /* Pairs are numbered i = t*k + j. counts[e] = pairs routed to e. Each
  * expert's segment is padded up to a multiple of block_m; offsets[e] is the

@@ -1,9 +1,8 @@
 """Write tests/golden/routing_hashes.json from the CPU oracle.
 
-Fixed-token and hash-based checks: the MI250 paper ("DeepSeek-V4-Flash on AMD
-gfx90a: Correctness Recovery and Inference Performance Engineering",
-abstract) establishes fixed-token and hash-based correctness checks before any
-optimization. This script records, for each seeded workload, SHA-256 digests
+The MI250 paper (DeepSeek-V4-Flash on AMD gfx90a: Correctness Recovery and
+Inference Performance Engineering, abstract) checks correctness on fixed
+tokens and with hashes before optimizing. This script records, for each seeded workload, SHA-256 digests
 of the oracle's routing ids (int32, little-endian, [T][k] row-major), routing
 weights (fp32 bits) and expert-sort arrays. It calls only ``oracle`` and the
 seeded input generators.
