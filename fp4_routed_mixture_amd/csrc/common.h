@@ -75,13 +75,15 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
 
-// int8 in [-8, 8] -> OCP FP8 E4M3 bit pattern (exact).
+// int8 in [-8, 8] -> OCP FP8 E4M3 bit pattern (exact). For 1 <= a <= 8 the
+// fp32 encoding of a has exponent field 127 + e and a mantissa whose top
+// three bits are E4M3's mantissa; E4M3 wants exponent field 7 + e, so the
+// code is (fp32 bits >> 20) - (120 << 3). Pure ALU: a lookup table would be
+// read from memory on every call.
 __device__ __forceinline__ uint32_t small_int_to_e4m3(int v) {
-  uint32_t s = v < 0 ? 0x80u : 0u;
-  int a = v < 0 ? -v : v;
-  // 0, 1, 2, 3, 4, 5, 6, 7, 8
-  const uint32_t tab[9] = {0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50};
-  return a == 0 ? 0u : (s | tab[a]);
+  const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+  const uint32_t mag = a ? (__float_as_uint((float)a) >> 20) - 960u : 0u;
+  return (v < 0 ? 0x80u : 0u) | mag;
 }
 
 // Split an int8 value q in [-127, 127] into hi, lo with q = 16 * hi + lo,

@@ -18,6 +18,9 @@
 // desc, expert asc); w_j = s_j / S with S accumulated left to right in slot
 // order.
 //
+// Small batches keep the 64 chunk sums chunk-minor ([T][E][64]) so that the
+// finishing kernel reads each logit's sums as one 256-byte run.
+//
 // Small batches (T <= 64) keep all 64 chunk sums (one chunk per workgroup, so
 // each workgroup loads its operands once) and finish the whole tree in
 // topk_quant_token, one workgroup per token, which also quantizes the token's
@@ -165,20 +168,35 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const int e = e0 + tx * RB + b;
-      if (e < E) partial[((size_t)slice * T + t) * E + e] = st2[a][b];
+      if (e < E) {
+        if (CPS == 1)
+          partial[((size_t)t * E + e) * 64 + slice] = st2[a][b];  // chunk-minor: one 256-byte run per logit
+        else
+          partial[((size_t)slice * T + t) * E + e] = st2[a][b];
+      }
     }
   }
 }
 
 // Logit of (t, e): the remaining tree levels over the NS slice sums (a
-// perfect pairwise tree in index order), then the bias.
+// perfect pairwise tree in index order), then the bias. NS = 64 reads the
+// chunk-minor layout [T][E][64], NS = 8 the slice-major layout [8][T][E].
 template <int NS>
 __device__ __forceinline__ float finish_logit(const float* __restrict__ partial, const float* __restrict__ bias, int T,
                                               int E, int t, int e) {
-  const size_t st = (size_t)T * E, o = (size_t)t * E + e;
   float v[NS];
+  if (NS == 64) {
+    const float4* p = reinterpret_cast<const float4*>(partial + ((size_t)t * E + e) * 64);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
+    for (int i = 0; i < NS / 4; ++i) {
+      const float4 q = p[i];
+      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+  } else {
+    const size_t st = (size_t)T * E, o = (size_t)t * E + e;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
+  }
 #pragma unroll
   for (int w = NS; w > 1; w >>= 1)
 #pragma unroll
@@ -251,26 +269,44 @@ __device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K
   }
 }
 
-// Rank-based top-k over the scores of one token held in LDS: the rank of
-// expert e is the number of experts that come before it in the order (score
-// desc, expert asc); the experts with rank < K are the selection and the rank
-// is the slot. No cross-lane reductions, and the same result as K rounds of
-// argmax. `stride`/`first` split the experts over the calling threads; every
-// selected expert writes its slot of sel_id / sel_s.
-__device__ __forceinline__ void rank_select(const float* __restrict__ sc, int E, int K, int first, int stride,
-                                            int* sel_id, float* sel_s) {
+// Top-k of one token's scores (sc[0..E), E <= 1024, scores >= 0) by one
+// wave: K rounds of a wave argmax keyed (score desc, expert asc), the same
+// selection and slot order as a full sort. Lane l keeps experts l, l+64, ...
+// in registers; a selected expert's score is replaced by -1 (below every
+// sigmoid score). Lane 0 writes slot j of sel_id / sel_s.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, int K, int* sel_id, float* sel_s) {
+  const int lane = threadIdx.x & 63;
+  float s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    s[i] = e < E ? sc[e] : -1.0f;
+  }
 #pragma unroll 1
-  for (int e = first; e < E; e += stride) {
-    const float me = sc[e];
-    int rank = 0;
-#pragma unroll 4
-    for (int f = 0; f < E; ++f) {
-      const float o = sc[f];
-      rank += (o > me) || (o == me && f < e);
+  for (int j = 0; j < K; ++j) {
+    float bv = s[0];
+    int be = lane;
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+      if (s[i] > bv) {  // strictly greater: the lower expert wins a tie
+        bv = s[i];
+        be = lane + 64 * i;
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
     }
-    if (rank < K) {
-      sel_id[rank] = e;
-      sel_s[rank] = me;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (lane + 64 * i == be) s[i] = -1.0f;
+    if (lane == 0) {
+      sel_id[j] = be;
+      sel_s[j] = bv;
     }
   }
 }
@@ -323,7 +359,7 @@ __global__ __launch_bounds__(256) void topk_quant_token_kernel(const float* __re
     if (lane == 0) red[wave] = amax;
   }
   __syncthreads();
-  rank_select(sc, E, K, tid, 256, sel_id, sel_s);
+  if (wave == 0) wave_topk(sc, E, K, sel_id, sel_s);
   __syncthreads();
   if (tid < K) {
     ids_out[(size_t)t * K + tid] = sel_id[tid];
@@ -382,7 +418,7 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  rank_select(sc[wave], E, K, lane, 64, sel_id[wave], sel_s[wave]);
+  wave_topk(sc[wave], E, K, sel_id[wave], sel_s[wave]);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
