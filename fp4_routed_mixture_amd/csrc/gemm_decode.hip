@@ -10,8 +10,8 @@
 // representable dyadic rational, so the block-scaled sum is exact and equals
 // the integer block sums of the definition.
 //
-// Work item: (row tile j of 32 weight rows -- a gate/up tile pair for W13 --,
-// sort tile q of 16 pairs of one expert). B columns 0..15 are the hi parts of
+// Work item: (two 32-row weight tiles -- a gate/up tile pair of W13, or two
+// consecutive row tiles of W2 --, sort tile q of 16 pairs of one expert). B columns 0..15 are the hi parts of
 // the 16 pair rows, 16..31 the lo parts. The four waves of a workgroup split
 // K into contiguous ranges of four-K-tile groups and reduce through LDS in a
 // fixed order. Weights stream straight from HBM into MFMA registers: the
@@ -53,11 +53,15 @@ __device__ __forceinline__ v4i ld_weights(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
+// S = 2: a second 32-row tile, the up half of a W13 tile pair (interleaved
+// per K-step: a_step = 2048, a1 at +1024, scales at +64 dwords) or the next
+// W2 row tile (a_step = 1024, a1 at +KT*1024, scales at +G*64 dwords).
 template <int S>
 __device__ __forceinline__ void load_group(Group<S>& G, const uint8_t* aptr, const uint32_t* sptr, const uint8_t* bptr,
-                                           bool valid, int g, int KT) {
-  G.sa0 = sptr[(size_t)g * S * 64];
-  G.sa1 = S == 2 ? sptr[(size_t)g * S * 64 + 64] : 0u;
+                                           bool valid, int g, int KT, uint32_t a_step, uint32_t a1_off,
+                                           uint32_t s_step, uint32_t s1_off) {
+  G.sa0 = sptr[(size_t)g * s_step];
+  G.sa1 = S == 2 ? sptr[(size_t)g * s_step + s1_off] : 0u;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int kt = g * 4 + u;
@@ -65,8 +69,8 @@ __device__ __forceinline__ void load_group(Group<S>& G, const uint8_t* aptr, con
     G.a1[u] = (v4i){0, 0, 0, 0};
     G.b[u] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
     if (kt < KT) {
-      G.a0[u] = ld_weights(aptr + (size_t)kt * S * 1024);
-      if (S == 2) G.a1[u] = ld_weights(aptr + (size_t)kt * S * 1024 + 1024);
+      G.a0[u] = ld_weights(aptr + (size_t)kt * a_step);
+      if (S == 2) G.a1[u] = ld_weights(aptr + (size_t)kt * a_step + a1_off);
       if (valid) {
         const v4i lo = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64);
         const v4i hi = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64 + 32);
@@ -93,7 +97,9 @@ __device__ __forceinline__ void mma_group(const Group<S>& G, v16f& acc0, v16f& a
 
 // Main loop + cross-wave reduction. On return red[w][s][v][lane] holds every
 // wave's partial sums (read by the epilogue after __syncthreads()).
-template <int S>
+// PAIRED: the two tiles are a W13 gate/up pair (tile pair j of NT pairs);
+// otherwise S tiles S*j .. S*j+S-1 of the NT row tiles of W2.
+template <int S, bool PAIRED>
 __device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
                                                 const uint8_t* __restrict__ act8, int row, bool valid, int part, int e,
                                                 int j, int K, int NT, float (*red)[S][16][64]) {
@@ -102,14 +108,17 @@ __device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, 
   const int h = lane >> 5;
   const uint8_t* bptr = act8 + ((size_t)row * 2 + part) * K + h * 16;
   const uint32_t sb = part ? 0x7f7f7f7fu : 0x83838383u;  // lo: 2^0, hi: 2^4
-  const size_t tile = (size_t)e * NT + j;
-  const uint8_t* aptr = wq + tile * KT * (S * 1024) + lane * 16;
-  const uint32_t* sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (S * 256)) + lane;
+  constexpr int TS = PAIRED ? 2 : 1;  // 32-row tiles per NT unit
+  const size_t tile = (size_t)e * NT + (PAIRED ? j : (size_t)S * j);
+  const uint8_t* aptr = wq + tile * KT * (TS * 1024) + lane * 16;
+  const uint32_t* sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (TS * 256)) + lane;
+  const uint32_t a_step = TS * 1024, a1_off = PAIRED ? 1024u : (uint32_t)KT * 1024;
+  const uint32_t s_step = TS * 64, s1_off = PAIRED ? 64u : (uint32_t)G * 64;
   const int g0 = (G * wave) / NW, g1 = (G * (wave + 1)) / NW;
   v16f acc0 = {}, acc1 = {};
   for (int g = g0; g < g1; ++g) {
     Group<S> cur;
-    load_group<S>(cur, aptr, sptr, bptr, valid, g, KT);
+    load_group<S>(cur, aptr, sptr, bptr, valid, g, KT, a_step, a1_off, s_step, s1_off);
     mma_group<S>(cur, acc0, acc1, sb);
   }
 #pragma unroll
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
   const int pair = sorted[q * DM + (c & 15)];
   const bool valid = pair < P;
   const int row = valid ? pair / top_k : 0;
-  decode_mainloop<2>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
+  decode_mainloop<2, true>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
 
   // a = (g * sigmoid(g)) * u for the hi-column lanes' rows
   const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
@@ -165,15 +174,15 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ aq8,
     const float* __restrict__ as, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
     const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ y, int H) {
-  __shared__ float red[NW][1][16][64];
-  const int j = blockIdx.x, q = blockIdx.y;
+  __shared__ float red[NW][2][16][64];
+  const int j = blockIdx.x, q = blockIdx.y;  // j: pair of row tiles 2j, 2j+1
   if (q >= *n_tiles) return;
   const int e = tile_expert[q];
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, part = c >> 4;
   const int p = q * DM + (c & 15);
   const bool valid = sorted[p] < P;
-  decode_mainloop<1>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
+  decode_mainloop<2, false>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
 
   const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
   if ((l & 31) >= 16) return;
@@ -181,12 +190,14 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
   const int opair = sorted[op];
   if (opair >= P) return;
   const float s = as[op];
-  float* yrow = y + (size_t)opair * H + j * 32;
+  float* yrow = y + (size_t)opair * H + j * 64;
 #pragma unroll
-  for (int vv = 0; vv < 4; ++vv) {
-    const int v = vq * 4 + vv;
-    yrow[8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = s * reduced<1>(red, 0, v, l);
-  }
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      const int v = vq * 4 + vv;
+      yrow[t * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = s * reduced<2>(red, t, v, l);
+    }
 }
 
 // int8 requantization of the activation rows of the valid pairs: one
@@ -278,7 +289,7 @@ hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
                              int H, int I, int top_k, int P, float* y, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
-  dim3 grid(H / 32, max_tiles);
+  dim3 grid(H / 64, max_tiles);  // two 32-row tiles per workgroup (H % 256 == 0)
   decode_down_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32, top_k, P, y,
                                                H);
   return hipGetLastError();
