@@ -204,10 +204,31 @@ int moe_quantize(const moe_config* cfg, int32_t rows, int32_t K, int32_t in_dtyp
   return MOE_OK;
 }
 
+namespace {
+// The layer; with combine == false it stops after the down GEMM, leaving y
+// (per pair) and the routing weights in the workspace (the stack fuses the
+// combine with the residual update and the next layer's RMSNorm).
+int forward_impl(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                 const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
+                 int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
+                 size_t workspace_bytes, void* stream, bool combine);
+}  // namespace
+
 int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                      const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
                      float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  return forward_impl(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
+                      taps, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+int forward_impl(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                 const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
+                 int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
+                 size_t workspace_bytes, void* stream, bool combine) {
   int st = check_shape(cfg);
   if (st) return st;
   if (cfg->T == 0) return MOE_OK;
@@ -272,7 +293,7 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
                                H / 32, k, P, 0, nullptr, nullptr, y, H, s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
-    MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
+    if (combine) MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   } else {
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
@@ -287,7 +308,7 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
                               s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
-    MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
+    if (combine) MOE_TRY(moe_k_combine(y, w, T, H, k, out, s));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   }
 
@@ -318,6 +339,9 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
   }
   return MOE_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int moe_forward(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                 const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
@@ -355,13 +379,19 @@ int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* c
   hipStream_t s = (hipStream_t)stream;
   float* xn = at<float>(workspace, fw);
   float* ybuf = at<float>(workspace, fw + up256(nb));
+  const Plan p = make_plan(cfg);
+  const float* ypair = at<float>(workspace, p.y);
+  const float* wts = at<float>(workspace, p.w);
+  // x_{l+1} = x_l + moe_l(rmsnorm(x_l)): the first RMSNorm stands alone, each
+  // layer's combine, residual update and the next layer's RMSNorm are fused
+  MOE_TRY(moe_k_rmsnorm(x, cfg->T, cfg->H, xn, s));
   for (int l = 0; l < L; ++l) {
     float* yl = layer_out ? layer_out + (size_t)l * cfg->T * cfg->H : ybuf;
-    MOE_TRY(moe_k_rmsnorm(x, cfg->T, cfg->H, xn, s));
-    st = moe_forward_taps(cfg, xn, router_w[l], router_bias ? router_bias[l] : nullptr, w13[l], w13_scale[l], w2[l],
-                          w2_scale[l], yl, nullptr, nullptr, nullptr, workspace, fw, stream);
+    st = forward_impl(cfg, xn, router_w[l], router_bias ? router_bias[l] : nullptr, w13[l], w13_scale[l], w2[l],
+                      w2_scale[l], yl, nullptr, nullptr, nullptr, workspace, fw, stream, false);
     if (st) return st;
-    MOE_TRY(moe_k_residual(x, yl, (int64_t)cfg->T * cfg->H, s));
+    MOE_TRY(moe_k_combine_residual_norm(ypair, wts, cfg->T, cfg->H, cfg->top_k, x, layer_out ? yl : nullptr,
+                                        l + 1 < L ? xn : nullptr, s));
   }
   return MOE_OK;
 }

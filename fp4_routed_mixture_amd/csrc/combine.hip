@@ -6,6 +6,7 @@
 //   rmsnorm : out = x / sqrt(ss / H + 1e-6), ss in the router's fixed order
 //             (64 chunk chains, pairwise tree), one wave per row.
 //   residual: x += y.
+//   combine_residual_norm: the three above fused for stacked layers.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,6 +49,63 @@ __global__ __launch_bounds__(256) void residual_kernel(float* __restrict__ x, co
     x[i] = x[i] + y[i];
 }
 
+// Stacked layers: the combine of layer l, the residual update and the RMSNorm
+// of layer l+1's input in one pass per token (one 256-thread workgroup per
+// token), with the arithmetic of combine_kernel, residual_kernel and
+// rmsnorm_kernel in sequence:
+//   out = fma chain over slots of w_j * y_j   (stored to layer_out if given)
+//   x   = x + out
+//   xn  = x / sqrt(ss / H + 1e-6)              (if xn is given)
+// The updated row is kept in LDS with one pad float per 64 so that the 64
+// chunk chains of the sum of squares read distinct banks.
+__global__ __launch_bounds__(256) void combine_residual_norm_kernel(const float* __restrict__ y,
+                                                                    const float* __restrict__ w, int H, int K,
+                                                                    float* __restrict__ x, float* __restrict__ layer_out,
+                                                                    float* __restrict__ xn) {
+  extern __shared__ float row[];  // H + H/64 floats
+  __shared__ float r_sh;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* wt = w + (size_t)t * K;
+  float* xr = x + (size_t)t * H;
+  for (int n = tid * 4; n < H; n += 1024) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < K; ++j) {
+      const float wj = wt[j];
+      const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * K + j) * H + n);
+      acc.x = __builtin_fmaf(wj, v.x, acc.x);
+      acc.y = __builtin_fmaf(wj, v.y, acc.y);
+      acc.z = __builtin_fmaf(wj, v.z, acc.z);
+      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+    }
+    if (layer_out) *reinterpret_cast<float4*>(layer_out + (size_t)t * H + n) = acc;
+    float4 xv = *reinterpret_cast<const float4*>(xr + n);
+    xv.x = xv.x + acc.x;
+    xv.y = xv.y + acc.y;
+    xv.z = xv.z + acc.z;
+    xv.w = xv.w + acc.w;
+    *reinterpret_cast<float4*>(xr + n) = xv;
+    float* rr = row + n + (n >> 6);
+    rr[0] = xv.x; rr[1] = xv.y; rr[2] = xv.z; rr[3] = xv.w;
+  }
+  if (!xn) return;
+  __syncthreads();
+  if (tid < 64) {
+    const int L = H >> 6;
+    float p = 0.0f;
+    for (int i = 0; i < L; ++i) {
+      const int el = tid * L + i;  // element el sits at el + el / 64
+      const float v = row[el + (el >> 6)];
+      p = __builtin_fmaf(v, v, p);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) p = p + __shfl_xor(p, o, 64);
+    if (tid == 0) r_sh = __builtin_sqrtf(p / (float)H + 1e-6f);
+  }
+  __syncthreads();
+  const float r = r_sh;
+  for (int n = tid; n < H; n += 256) xn[(size_t)t * H + n] = row[n + (n >> 6)] / r;
+}
+
 int grid_for(size_t n) {
   size_t b = (n + 255) / 256;
   return (int)(b < 65536 ? (b ? b : 1) : 65536);
@@ -70,5 +128,22 @@ hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t s
 hipError_t moe_k_residual(float* x, const float* y, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   residual_kernel<<<grid_for((size_t)n), 256, 0, st>>>(x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, int H, int K, float* x,
+                                       float* layer_out, float* xn, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const size_t lds = (size_t)(H + H / 64) * 4;
+  // above 64 KB of dynamic LDS a kernel must opt in; static LDS (r_sh) counts
+  // against the same 160 KB, so ask for what H <= 16384 needs
+  static bool lds_opt_in = false;
+  if (!lds_opt_in) {
+    const hipError_t e = hipFuncSetAttribute((const void*)combine_residual_norm_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (16384 + 256) * 4);
+    if (e != hipSuccess) return e;
+    lds_opt_in = true;
+  }
+  combine_residual_norm_kernel<<<T, 256, lds, st>>>(y, w, H, K, x, layer_out, xn);
   return hipGetLastError();
 }

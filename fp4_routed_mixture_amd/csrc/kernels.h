@@ -60,3 +60,5 @@ hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc
 hipError_t moe_k_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st);
 hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t st);
 hipError_t moe_k_residual(float* x, const float* y, int64_t n, hipStream_t st);
+hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, int H, int K, float* x,
+                                       float* layer_out, float* xn, hipStream_t st);
