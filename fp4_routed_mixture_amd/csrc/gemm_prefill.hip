@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   constexpr int S = GATE_UP ? 2 : 1;           // 32-row tiles per NT unit (gate/up pair or one W2 tile)
   constexpr int UPW = WTW / S;                 // NT units per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][B_STAGE];
+  __shared__ uint32_t lds_s[BM * (16384 / 128 + 1)];  // pair-row scales, K <= 16384
+  __shared__ int lds_row[BM];
   const int nb = blockIdx.x, q = blockIdx.y;
   if (q >= *n_tiles) return;
   const int e = tile_expert[q];
@@ -111,14 +113,20 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     const int row = pr < P ? (rows_are_tokens ? pr / top_k : q * BM + br) : 0;  // padding reads row 0
     b_off[m] = (uint32_t)row * (uint32_t)(K >> 1) + c4 * 16;
   }
-  // scale-row offsets of this lane's pair rows (one per pair tile)
-  uint32_t sb_off[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int r = u * 32 + c;
-    const int pr = sorted[q * BM + r];
-    const int row = pr < P ? (rows_are_tokens ? pr / top_k : q * BM + r) : 0;
-    sb_off[u] = (uint32_t)row * (uint32_t)KB;
+  // The pair rows' E8M0 scales (K/32 bytes a row) are staged in LDS once:
+  // read in the main loop straight from global memory, every lane would
+  // touch its own cache line per load (one gathered row per lane), which
+  // costs the vector memory path more than the weight stream. Row stride
+  // K/128 + 1 dwords keeps the per-lane reads on distinct banks.
+  const int KD = K >> 7;  // scale dwords per row
+  if (tid < BM) {
+    const int pr = sorted[q * BM + tid];
+    lds_row[tid] = pr < P ? (rows_are_tokens ? pr / top_k : q * BM + tid) : 0;  // padding reads row 0
+  }
+  __syncthreads();
+  for (int i = tid; i < BM * KD; i += NWAVE * 64) {
+    const int r = i / KD, d = i - r * KD;
+    lds_s[r * (KD + 1) + d] = reinterpret_cast<const uint32_t*>(act_scales + (size_t)lds_row[r] * KB)[d];
   }
 
   v16f acc[WTW][NU];
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     for (int u = 0; u < NU; ++u) {
       // a group's 8 bytes; when K % 256 == 128 the last group has only 2
       // K-steps and its second dword is never selected (re-read the first)
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(act_scales + sb_off[u] + g * 8);
+      const uint32_t* p = lds_s + (u * 32 + c) * (KD + 1) + 2 * g;
       dx[u] = p[0];
       dy[u] = p[(4 * g + 2 < KT) ? 1 : 0];
     }
@@ -200,14 +208,15 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     }
   };
 
-  // prologue: scale group 0, K-steps 0..PF-1, pair-row stages 0 (stored) and 1
-  load_scales(sa, sx, sy, 0);
+  // prologue: K-steps 0..PF-1, pair-row stages 0 (stored) and 1, then
+  // scale group 0 (the barrier also publishes the staged pair-row scales)
 #pragma unroll
   for (int j = 0; j < PF; ++j) aload(j, j);
   bload(0, 0);
   bload(1, 1);
   bstore(0, 0);
   __syncthreads();
+  load_scales(sa, sx, sy, 0);
   // group g = K-steps 4g..4g+3 = stages 2g (buffer 0) and 2g+1 (buffer 1);
   // K-step kt sits in ring slot kt % PF
   using I0 = std::integral_constant<int, 0>;
