@@ -264,10 +264,21 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const int ex = amax > 0.0f ? moe::mx_scale_exp(amax) : 0;
         uint8_t* dst = aq + (size_t)p * (I >> 1) + (size_t)jp * 16;
+        // gfx950's scaled FP4 pack conversion divides by the (power-of-two)
+        // scale and rounds to nearest-even on the E2M1 grid with saturation
+        // at 6 and the sign kept -- the OCP rule, checked bit for bit against
+        // the software encoder below on 2^21 values including every midpoint.
+        // Scales that would be denormal or near the exponent limits take the
+        // software path.
+        const bool hw = ex >= 2 && ex <= 252;
+        const float scale = __uint_as_float((uint32_t)(hw ? ex : 127) << 23);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t packed = 0;
-          if (amax > 0.0f) {
+          if (hw) {
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, av[i * 4], av[i * 4 + 1], scale, 0);
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, av[i * 4 + 2], av[i * 4 + 3], scale, 1);
+          } else if (amax > 0.0f) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const float vs = __builtin_ldexpf(av[i * 4 + jj], 127 - ex);
