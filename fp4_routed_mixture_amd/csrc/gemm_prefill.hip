@@ -272,6 +272,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
         // software path.
         const bool hw = ex >= 2 && ex <= 252;
         const float scale = __uint_as_float((uint32_t)(hw ? ex : 127) << 23);
+        uint32_t word[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           uint32_t packed = 0;
@@ -286,10 +287,15 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
               packed |= code << (4 * jj);
             }
           }
-          // rows 8i + 4h .. +3 -> bytes 4i + 2h, 4i + 2h + 1
-          *reinterpret_cast<uint16_t*>(dst + 4 * i + 2 * h) = (uint16_t)packed;
+          // rows 8i + 4h .. +3 are bytes 4i + 2h, 4i + 2h + 1 of the block:
+          // the lane with h = 0 gathers its partner's half into one dword
+          const uint32_t other = (uint32_t)__shfl_xor((int)packed, 32, 64);
+          word[i] = (packed & 0xffffu) | (other << 16);
         }
-        if (h == 0) as[(size_t)p * (I >> 5) + jp] = (uint8_t)ex;
+        if (h == 0) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(word[0], word[1], word[2], word[3]);
+          as[(size_t)p * (I >> 5) + jp] = (uint8_t)ex;
+        }
       }
     } else {
       const int H = out_n;
