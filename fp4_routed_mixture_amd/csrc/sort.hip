@@ -75,20 +75,48 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
   int* offs = tot + E;        // E + 1
   int* tmp = offs + E + 1;    // 1024
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
+  // Per expert, an exclusive scan over the blocks. With E <= 256 each expert
+  // gets 1024 / E' threads (E' = E rounded up to a power of two) that scan
+  // contiguous runs of blocks, then add the sums of the runs before them.
+  int split = 1;
+  while (split * 2 * E <= 1024 && split < 16) split *= 2;
+  int* part = tmp;  // 1024 run sums
+  {
+    const int e = tid / split, r = tid % split;
+    const int b0 = (nblocks * r) / split, b1 = (nblocks * (r + 1)) / split;
     int run = 0;
-    for (int b = 0; b < nblocks; ++b) {
-      int c = block_hist[(size_t)b * E + e];
-      block_hist[(size_t)b * E + e] = run;
-      run += c;
+    if (e < E)
+      for (int b = b0; b < b1; ++b) run += block_hist[(size_t)b * E + e];
+    part[tid] = run;
+    __syncthreads();
+    int base = 0, total = 0;
+    if (e < E) {
+      for (int i = 0; i < split; ++i) {
+        const int v = part[e * split + i];
+        if (i < r) base += v;
+        total += v;
+      }
+      if (r == 0) tot[e] = total;
     }
-    tot[e] = run;
+    __syncthreads();  // part[] is reused by scan_offsets
+    if (e < E) {
+      run = base;
+      for (int b = b0; b < b1; ++b) {
+        const int c = block_hist[(size_t)b * E + e];
+        block_hist[(size_t)b * E + e] = run;
+        run += c;
+      }
+    }
   }
   __syncthreads();
   moe::scan_offsets(tot, E, block_m, offs, tmp);
-  for (int e = tid; e < E; e += blockDim.x) {
-    counts[e] = tot[e];
-    for (int b = 0; b < nblocks; ++b) block_hist[(size_t)b * E + e] += offs[e];
+  {
+    const int e = tid / split, r = tid % split;
+    const int b0 = (nblocks * r) / split, b1 = (nblocks * (r + 1)) / split;
+    if (e < E) {
+      if (r == 0) counts[e] = tot[e];
+      for (int b = b0; b < b1; ++b) block_hist[(size_t)b * E + e] += offs[e];
+    }
   }
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);

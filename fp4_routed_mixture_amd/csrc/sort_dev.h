@@ -56,20 +56,30 @@ __device__ inline void block_rank(int my_id, bool my_valid, int E, int* wcnt, in
 }
 
 // Block-wide exclusive scan of padded counts over E experts (E <= 1024,
-// 1024 threads): writes offsets[0..E].
+// blockDim.x == 1024): writes offsets[0..E]. A scan inside each wave
+// (shuffles), the wave totals scanned by wave 0, then one add: two barriers.
 __device__ inline void scan_offsets(const int* counts_lds, int E, int block_m, int* offs_lds, int* tmp) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int v = 0;
   if (tid < E) v = (counts_lds[tid] + block_m - 1) / block_m * block_m;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int add = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
   }
-  if (tid < E) offs_lds[tid + 1] = tmp[tid];
+  if (lane == 63) tmp[wave] = v;  // inclusive wave totals
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < 16 ? tmp[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int n = __shfl_up(t, o, 64);
+      if (lane >= o) t += n;
+    }
+    if (lane < 16) tmp[16 + lane] = t - tmp[lane];  // exclusive base of each wave
+  }
+  __syncthreads();
+  if (tid < E) offs_lds[tid + 1] = v + tmp[16 + wave];
   if (tid == 0) offs_lds[0] = 0;
   __syncthreads();
 }
