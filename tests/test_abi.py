@@ -116,3 +116,29 @@ def test_other_entry_point_errors(L):
     assert L.moe_rmsnorm(2, 128, FAKE, FAKE + 4, None) == 4
     assert L.moe_residual_add(-1, FAKE, FAKE, None) == 1
     assert L.moe_residual_add(0, None, None, None) == 0
+
+
+def test_stack_entry_point_errors(L):
+    c = cfg(x_dtype=0)
+    n = C.c_size_t(0)
+    assert L.moe_stack_workspace_size(C.byref(c), C.byref(n)) == 0
+    fwd_ws = C.c_size_t(0)
+    assert L.moe_workspace_size(C.byref(c), C.byref(fwd_ws)) == 0
+    assert n.value >= fwd_ws.value + 2 * c.T * c.H * 4  # normalized stream + per-layer output
+    P = C.c_void_p
+    one = (P * 1)(FAKE)
+    arr = C.cast(one, P)
+
+    def stack(cc, L_=1, x=FAKE + (1 << 32), ptrs=arr, ws=FAKE + (1 << 34), ws_bytes=1 << 40, out=None):
+        return L.moe_forward_stack(C.byref(cc), L_, x, ptrs, None, ptrs, ptrs, ptrs, ptrs, out, ws, ws_bytes, None)
+
+    assert stack(c, L_=-1) == 1
+    assert stack(c, L_=0) == 0                      # no layers: nothing to do
+    assert stack(cfg(x_dtype=1)) == 2               # the residual stream is fp32
+    assert stack(c, x=None) == 1
+    assert stack(c, ptrs=None) == 1
+    assert stack(c, ws_bytes=n.value - 1) == 5
+    assert stack(c, x=FAKE + (1 << 32) + 4) == 3    # misaligned stream
+    null_layer = C.cast((P * 1)(None), P)
+    assert stack(c, ptrs=null_layer) == 1           # a layer without weights
+    assert stack(c, ws=FAKE + (1 << 32)) == 4       # workspace overlaps the stream

@@ -1,0 +1,51 @@
+"""GPU parity at the shape limits the C ABI accepts: the most experts and the
+largest top-k (E = 1024, k = 16), the largest K of each GEMM (H = 16384 for
+gate/up, I = 16384 for down), and a batch of one token, in both activation
+modes. int8 mode must match the oracle bit for bit, MXFP4 within the
+tolerance; routing always bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from fp4_routed_mixture_amd import synth as S
+from fp4_routed_mixture_amd import synth_device as SD
+from gpu_util import assert_close_rms, oracle_layer, require_gpu, run_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+CASES = [
+    # name, T, H, I, E, k
+    ("max_experts_topk", 24, 256, 128, 1024, 16),
+    ("max_h", 9, 16384, 256, 4, 2),
+    ("max_i", 9, 256, 16384, 4, 2),
+    ("one_token", 1, 4096, 2048, 256, 6),
+]
+
+
+@pytest.mark.parametrize("act_mode", [S.ACT_INT8, S.ACT_MXFP4])
+@pytest.mark.parametrize("name,T,H,I,E,k", CASES)
+def test_shape_limits(name, T, H, I, E, k, act_mode):
+    w = S.Workload(name, T, H, I, E, k, S.X_BF16, act_mode, False, 31)
+    print(f"[limits] {S.describe(w)}", flush=True)
+    layer = SD.load_layer(w)
+    g = run_forward(w, layer, SD.activations(w), taps=True)
+    o = oracle_layer(w, S.activations(w), intermediates=True)
+    assert np.array_equal(g["ids"], o["ids"])
+    assert np.array_equal(g["w"].view(np.uint32), o["w"].view(np.uint32))
+    # every id distinct per token, weights sum to 1 within k ulps
+    assert all(len(set(r)) == k for r in g["ids"].tolist())
+    assert np.all(np.abs(g["w"].astype(np.float64).sum(1) - 1.0) <= k * 2.0 ** -23)
+    if act_mode == S.ACT_INT8:
+        assert np.array_equal(g["out"], o["out"])
+    else:
+        assert int((g["aq"] != o["aq"]).sum()) == 0
+        assert_close_rms(g["out"], o["out"])
+    del layer
