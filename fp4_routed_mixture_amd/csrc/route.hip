@@ -70,8 +70,10 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
   constexpr int TT = 16 * RA, TE = 16 * RB;
   constexpr int NX = TT * KS / 4 / 256, NW = TE * KS / 4 / 256;  // float4 groups per thread
   static_assert(NX >= 1 && NW >= 1, "tile too small for the stage");
-  __shared__ float xs[KS][TT + 1];
-  __shared__ float ws[KS][TE + 1];
+  // rows padded to a 16-byte multiple: each thread reads its RA (RB) operands
+  // of one k as 16-byte LDS loads, the 16 lanes of a row group contiguous
+  __shared__ __attribute__((aligned(16))) float xs[KS][TT + 4];
+  __shared__ __attribute__((aligned(16))) float ws[KS][TE + 4];
   const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, slice = blockIdx.z;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int L = H >> 6;
@@ -124,10 +126,26 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
 #pragma unroll 4
     for (int kk = 0; kk < KS; ++kk) {
       float xa[RA], wb[RB];
+      if constexpr (RA % 4 == 0) {
 #pragma unroll
-      for (int a = 0; a < RA; ++a) xa[a] = xs[kk][ty * RA + a];
+        for (int a = 0; a < RA; a += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(&xs[kk][ty * RA + a]);
+          xa[a] = v.x; xa[a + 1] = v.y; xa[a + 2] = v.z; xa[a + 3] = v.w;
+        }
+      } else {
 #pragma unroll
-      for (int b = 0; b < RB; ++b) wb[b] = ws[kk][tx * RB + b];
+        for (int a = 0; a < RA; ++a) xa[a] = xs[kk][ty * RA + a];
+      }
+      if constexpr (RB % 4 == 0) {
+#pragma unroll
+        for (int b = 0; b < RB; b += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(&ws[kk][tx * RB + b]);
+          wb[b] = v.x; wb[b + 1] = v.y; wb[b + 2] = v.z; wb[b + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) wb[b] = ws[kk][tx * RB + b];
+      }
 #pragma unroll
       for (int a = 0; a < RA; ++a)
 #pragma unroll
