@@ -31,7 +31,8 @@
 // Epilogue W13: a = (g * sigmoid(g)) * u, then MXFP4 requantization of each
 // 32-block along I (a 32-row gate tile is exactly one block): lanes l and
 // l^32 hold the block's two halves, one shuffle gives the block amax.
-// Epilogue W2: y[pair][H] in fp32.
+// Epilogue W2: y[pair][H] in fp32, transposed through LDS so that stores
+// write whole row segments.
 #include <type_traits>
 
 #include "common.h"
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][B_STAGE];
   __shared__ uint32_t lds_s[BM * (16384 / 128 + 1)];  // pair-row scales, K <= 16384
   __shared__ int lds_row[BM];
+  __shared__ int lds_pair[BM];
   const int nb = blockIdx.x, q = blockIdx.y;
   if (q >= *n_tiles) return;
   const int e = tile_expert[q];
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   if (tid < BM) {
     const int pr = sorted[q * BM + tid];
     lds_row[tid] = pr < P ? (rows_are_tokens ? pr / top_k : q * BM + tid) : 0;  // padding reads row 0
+    lds_pair[tid] = pr;
   }
   __syncthreads();
   for (int i = tid; i < BM * KD; i += NWAVE * 64) {
@@ -241,6 +244,43 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   if (NS & 1) stage(0, I0(), I0(), 0, false);  // last half group (K % 256 == 128)
 
   // ---- epilogue ------------------------------------------------------------
+  if (!GATE_UP) {
+    // y through LDS: each 32 x 32 tile goes in as the MFMA result layout and
+    // comes out row-contiguous, so a store instruction writes whole 128-byte
+    // row segments of 8 rows instead of 32-byte pieces of 32 rows. Each wave
+    // uses its own 4.5 KB of the scale-staging LDS, free after the barrier.
+    __syncthreads();
+    if (!w_valid) return;
+    float* stg = reinterpret_cast<float*>(lds_s) + wave * (32 * 36);
+    const int H = out_n;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      int prow[4];
+#pragma unroll
+      for (int sr = 0; sr < 4; ++sr) prow[sr] = lds_pair[u * 32 + (lane >> 3) + 8 * sr];
+#pragma unroll
+      for (int t = 0; t < WTW; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(&stg[c * 36 + 8 * i + 4 * h]) =
+              make_float4(acc[t][u][4 * i], acc[t][u][4 * i + 1], acc[t][u][4 * i + 2], acc[t][u][4 * i + 3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int sr = 0; sr < 4; ++sr) {
+          const int r = (lane >> 3) + 8 * sr;
+          const float4 v = *reinterpret_cast<const float4*>(&stg[r * 36 + (lane & 7) * 4]);
+          if (prow[sr] < P)
+            *reinterpret_cast<float4*>(y + (size_t)prow[sr] * H + (unit0 + t) * 32 + (lane & 7) * 4) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+    return;
+  }
   if (!w_valid) return;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
@@ -297,17 +337,6 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
           as[(size_t)p * (I >> 5) + jp] = (uint8_t)ex;
         }
       }
-    } else {
-      const int H = out_n;
-      float* yrow = y + (size_t)pair * H;
-#pragma unroll
-      for (int t = 0; t < WTW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = (unit0 + t) * 32 + 8 * i + 4 * h;
-          *reinterpret_cast<float4*>(yrow + n) =
-              make_float4(acc[t][u][4 * i], acc[t][u][4 * i + 1], acc[t][u][4 * i + 2], acc[t][u][4 * i + 3]);
-        }
     }
   }
 }
