@@ -21,11 +21,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < K; ++j) {
       const float wj = w[t * K + j];
-      const float4 v = *reinterpret_cast<const float4*>(y + (t * K + j) * (size_t)H + n);
-      acc.x = __builtin_fmaf(wj, v.x, acc.x);
-      acc.y = __builtin_fmaf(wj, v.y, acc.y);
-      acc.z = __builtin_fmaf(wj, v.z, acc.z);
-      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+      // y is read exactly once: keep it out of the caches
+      const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + (t * K + j) * (size_t)H + n));
+      acc.x = __builtin_fmaf(wj, v[0], acc.x);
+      acc.y = __builtin_fmaf(wj, v[1], acc.y);
+      acc.z = __builtin_fmaf(wj, v[2], acc.z);
+      acc.w = __builtin_fmaf(wj, v[3], acc.w);
     }
     *reinterpret_cast<float4*>(out + t * H + n) = acc;
   }
