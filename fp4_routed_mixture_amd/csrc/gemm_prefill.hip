@@ -33,6 +33,7 @@
 // l^32 hold the block's two halves, one shuffle gives the block amax.
 // Epilogue W2: y[pair][H] in fp32, transposed through LDS so that stores
 // write whole row segments.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   constexpr int S = GATE_UP ? 2 : 1;           // 32-row tiles per NT unit (gate/up pair or one W2 tile)
   constexpr int UPW = WTW / S;                 // NT units per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][B_STAGE];
-  __shared__ uint32_t lds_s[BM * (16384 / 128 + 1)];  // pair-row scales, K <= 16384
+  extern __shared__ uint32_t lds_s[];  // pair-row scales (BM x (K/128 + 1) dwords), later the y staging
   __shared__ int lds_row[BM];
   __shared__ int lds_pair[BM];
   const int nb = blockIdx.x, q = blockIdx.y;
@@ -353,11 +354,26 @@ hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc
   // NT: tile pairs (W13) or row tiles (W2); a workgroup covers 8 pairs / 16 tiles
   const int per_wg = NWAVE * (gate_up ? WTW / 2 : WTW);
   dim3 grid((NT + per_wg - 1) / per_wg, max_tiles);
+  // dynamic LDS: the pair-row scales, or the down GEMM's y staging (4 waves
+  // x 32 rows x 36 floats), whichever is larger
+  const size_t lds = std::max<size_t>((size_t)BM * (K / 128 + 1) * 4, gate_up ? 0 : (size_t)NWAVE * 32 * 36 * 4);
+  // above 64 KB of dynamic LDS a kernel must opt in; the static arrays
+  // (pair-row stages, row maps) share the 160 KB
+  static bool lds_opt_in = false;
+  if (!lds_opt_in) {
+    const int cap = 160 * 1024 - 2 * B_STAGE - 2 * BM * 4 - 1024;
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+    if (e != hipSuccess) return e;
+    lds_opt_in = true;
+  }
   if (gate_up)
-    prefill_gemm_kernel<true><<<grid, 256, 0, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles, K,
+    prefill_gemm_kernel<true><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles, K,
                                                     NT, top_k, P, rows_are_tokens, aq, as, y, out_n);
   else
-    prefill_gemm_kernel<false><<<grid, 256, 0, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles,
+    prefill_gemm_kernel<false><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles,
                                                      K, NT, top_k, P, rows_are_tokens, aq, as, y, out_n);
   return hipGetLastError();
 }
