@@ -313,25 +313,35 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
         // software path.
         const bool hw = ex >= 2 && ex <= 252;
         const float scale = __uint_as_float((uint32_t)(hw ? ex : 127) << 23);
+        uint32_t packed[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          packed[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, av[i * 4], av[i * 4 + 1], scale, 0);
+          packed[i] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed[i], av[i * 4 + 2], av[i * 4 + 3], scale, 1);
+        }
+        // the software encoder only where a block's scale is out of the
+        // conversion's range; a wave-uniform test keeps it a real branch
+        if (__builtin_amdgcn_ballot_w64(!hw) != 0 && !hw) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            packed[i] = 0;
+            if (amax > 0.0f) {
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const float vs = __builtin_ldexpf(av[i * 4 + jj], 127 - ex);
+                const uint32_t code = moe::e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
+                packed[i] |= code << (4 * jj);
+              }
+            }
+          }
+        }
         uint32_t word[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          uint32_t packed = 0;
-          if (hw) {
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, av[i * 4], av[i * 4 + 1], scale, 0);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, av[i * 4 + 2], av[i * 4 + 3], scale, 1);
-          } else if (amax > 0.0f) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float vs = __builtin_ldexpf(av[i * 4 + jj], 127 - ex);
-              const uint32_t code = moe::e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
-              packed |= code << (4 * jj);
-            }
-          }
           // rows 8i + 4h .. +3 are bytes 4i + 2h, 4i + 2h + 1 of the block:
           // the lane with h = 0 gathers its partner's half into one dword
-          const uint32_t other = (uint32_t)__shfl_xor((int)packed, 32, 64);
-          word[i] = (packed & 0xffffu) | (other << 16);
+          const uint32_t other = (uint32_t)__shfl_xor((int)packed[i], 32, 64);
+          word[i] = (packed[i] & 0xffffu) | (other << 16);
         }
         if (h == 0) {
           *reinterpret_cast<uint4*>(dst) = make_uint4(word[0], word[1], word[2], word[3]);
