@@ -75,6 +75,37 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
 
+// One MXFP4 block: 32 values with block exponent e (amax > 0) -> 16 bytes of
+// E2M1 codes, value 2i in the low nibble of byte i. gfx950's scaled FP4 pack
+// conversion divides by the power-of-two scale 2^(e-127) and rounds as the
+// OCP rule above does (nearest-even, saturating at 6, sign kept: checked bit
+// for bit against e2m1_mag_code on 2^21 values including every midpoint);
+// scales outside its normal range take the compare ladder.
+__device__ __forceinline__ uint4 mx_pack32(const float* v, int e) {
+  uint32_t w[4];
+  if (e >= 2 && e <= 252) {
+    const float scale = __uint_as_float((uint32_t)e << 23);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[8 * i], v[8 * i + 1], scale, 0);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[8 * i + 2], v[8 * i + 3], scale, 1);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[8 * i + 4], v[8 * i + 5], scale, 2);
+      p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[8 * i + 6], v[8 * i + 7], scale, 3);
+      w[i] = p;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float vs = __builtin_ldexpf(v[i], 127 - e);
+      const uint32_t c = e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
+      w[i / 8] |= c << ((i % 8) * 4);
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // int8 in [-8, 8] -> OCP FP8 E4M3 bit pattern (exact). For 1 <= a <= 8 the
 // fp32 encoding of a has exponent field 127 + e and a mantissa whose top
 // three bits are E4M3's mantissa; E4M3 wants exponent field 7 + e, so the

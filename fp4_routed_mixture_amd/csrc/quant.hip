@@ -76,16 +76,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const XT* __restrict__
       amax = fmaxf(amax, fabsf(x[i]));
     }
     int e = amax > 0.0f ? moe::mx_scale_exp(amax) : 0;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (amax > 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float vs = __builtin_ldexpf(x[i], 127 - e);
-        uint32_t c = moe::e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
-        w[i / 8] |= c << ((i % 8) * 4);
-      }
-    }
-    *reinterpret_cast<uint4*>(codes + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(codes + b * 16) = amax > 0.0f ? moe::mx_pack32(x, e) : make_uint4(0, 0, 0, 0);
     scales[b] = (uint8_t)e;
   }
 }

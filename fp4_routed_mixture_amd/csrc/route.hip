@@ -272,16 +272,7 @@ __device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K
 #pragma unroll
       for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
       const int e = amax > 0.f ? moe::mx_scale_exp(amax) : 0;
-      uint32_t w[4] = {0, 0, 0, 0};
-      if (amax > 0.f) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float vs = __builtin_ldexpf(v[i], 127 - e);
-          const uint32_t c = moe::e2m1_mag_code(fabsf(vs)) | ((__float_as_uint(vs) >> 31) << 3);
-          w[i / 8] |= c << ((i % 8) * 4);
-        }
-      }
-      *reinterpret_cast<uint4*>(q + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(q + b * 16) = amax > 0.f ? moe::mx_pack32(v, e) : make_uint4(0, 0, 0, 0);
       qs[b] = (uint8_t)e;
     }
   }
