@@ -35,9 +35,13 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 # ----------------------------------------------------------------- HIP events
 class HipEvents:
+    # timing-only events: no system-scope fence (cache writeback/invalidate)
+    # when they are recorded, so that they disturb the measured kernels less
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def __init__(self):
         self.hip = C.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
@@ -46,7 +50,7 @@ class HipEvents:
         arr = (C.c_void_p * n)()
         for i in range(n):
             ev = C.c_void_p()
-            assert self.hip.hipEventCreate(C.byref(ev)) == 0
+            assert self.hip.hipEventCreateWithFlags(C.byref(ev), self.DISABLE_SYSTEM_FENCE) == 0
             arr[i] = ev
         return arr
 
