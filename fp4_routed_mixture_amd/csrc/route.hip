@@ -278,44 +278,63 @@ __device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K
   }
 }
 
+// Wave-wide max / min of a uint32 by DPP: row shifts build each 16-lane
+// row's prefix, the two row broadcasts carry it across rows, lane 63 ends with
+// the result (read back as a scalar). Lanes without a DPP source contribute
+// the operation's identity.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  const int ident = -1;  // 0xffffffff
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x111, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x112, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x114, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x118, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x142, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Top-k of one token's scores (sc[0..E), E <= 1024, scores >= 0) by one
 // wave: K rounds of a wave argmax keyed (score desc, expert asc), the same
 // selection and slot order as a full sort. Lane l keeps experts l, l+64, ...
-// in registers; a selected expert's score is replaced by -1 (below every
-// sigmoid score). Lane 0 writes slot j of sel_id / sel_s.
+// in registers as keys fp32 bits + 1 (scores are non-negative, so the bits
+// order like the values; 0 marks a taken or absent expert). A round is two
+// wave reductions: the largest key, then the lowest expert holding it.
+// Lane 0 writes slot j of sel_id / sel_s.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, int K, int* sel_id, float* sel_s) {
   const int lane = threadIdx.x & 63;
-  float s[16];
+  uint32_t key[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    s[i] = e < E ? sc[e] : -1.0f;
+    key[i] = e < E ? __float_as_uint(sc[e]) + 1u : 0u;
   }
 #pragma unroll 1
   for (int j = 0; j < K; ++j) {
-    float bv = s[0];
+    uint32_t bk = key[0];
     int be = lane;
 #pragma unroll
     for (int i = 1; i < 16; ++i)
-      if (s[i] > bv) {  // strictly greater: the lower expert wins a tie
-        bv = s[i];
+      if (key[i] > bk) {  // strictly greater: the lower expert wins a tie
+        bk = key[i];
         be = lane + 64 * i;
       }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    const uint32_t top = wave_umax(bk);
+    const int e = (int)wave_umin(bk == top ? (uint32_t)be : 0xffffffffu);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (lane + 64 * i == be) s[i] = -1.0f;
+      if (lane + 64 * i == e) key[i] = 0u;
     if (lane == 0) {
-      sel_id[j] = be;
-      sel_s[j] = bv;
+      sel_id[j] = e;
+      sel_s[j] = __uint_as_float(top - 1u);
     }
   }
 }

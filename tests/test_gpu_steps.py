@@ -184,3 +184,29 @@ def test_rmsnorm_and_residual_bitexact():
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.rmsnorm(xh).view(np.uint32))
     assert np.array_equal(x2.cpu().numpy(), (xh + y.cpu().numpy()).astype(np.float32))
+
+
+@pytest.mark.parametrize("T,E,k", [(3, 256, 6), (200, 256, 6), (5, 1024, 16), (70, 8, 8)])
+def test_topk_ties_go_to_lower_index(T, E, k):
+    """Exact score ties (zero router weights, a bias with repeated values and
+    scores that underflow to 0) are broken toward the lower expert index, and
+    the slots follow (score desc, expert asc), as in the oracle."""
+    H = 256
+    rng = np.random.default_rng(E + T)
+    x_h = rng.standard_normal((T, H)).astype(np.float32)
+    wr_h = np.zeros((E, H), np.float32)
+    levels = np.array([-200.0, -1.0, 0.0, 0.5, 0.5, 3.0], np.float32)
+    b_h = levels[rng.integers(0, len(levels), E)]
+    cfg = B.make_config(T, H, 128, E, k, S.X_F32, S.ACT_INT8)
+    ws = SD.workspace(cfg)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route(cfg, torch.from_numpy(x_h).cuda(), torch.from_numpy(wr_h).cuda(), torch.from_numpy(b_h).cuda(), ids,
+                wts, ws)
+    torch.cuda.synchronize()
+    ids_o, w_o = oracle.route(x_h, wr_h, b_h, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(wts.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+    # with every logit equal to its bias, the selection is the stable order
+    order = sorted(range(E), key=lambda e: (-float(b_h[e]), e))[:k]
+    assert all(list(r) == order for r in ids_o.tolist())
