@@ -301,7 +301,7 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
                                  P, a, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
-    MOE_TRY(moe_k_requant_rows(a, I, sorted, offsets + E, p.cap, P, aq, (float*)as, s));
+    MOE_TRY(moe_k_requant_rows(a, I, pos, P, aq, (float*)as, s));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
     MOE_TRY(moe_k_decode_down(w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, H, I, k, P, y,

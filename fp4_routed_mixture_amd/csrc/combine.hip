@@ -51,35 +51,44 @@ __global__ __launch_bounds__(256) void residual_kernel(float* __restrict__ x, co
 }
 
 // Stacked layers: the combine of layer l, the residual update and the RMSNorm
-// of layer l+1's input in one pass per token (one 256-thread workgroup per
-// token), with the arithmetic of combine_kernel, residual_kernel and
-// rmsnorm_kernel in sequence:
+// of layer l+1's input in one pass per token (one workgroup of min(H/4, 1024)
+// threads per token, a float4 column per thread and pass), with the
+// arithmetic of combine_kernel, residual_kernel and rmsnorm_kernel in sequence:
 //   out = fma chain over slots of w_j * y_j   (stored to layer_out if given)
 //   x   = x + out
 //   xn  = x / sqrt(ss / H + 1e-6)              (if xn is given)
-// The updated row is kept in LDS with one pad float per 64 so that the 64
-// chunk chains of the sum of squares read distinct banks.
-__global__ __launch_bounds__(256) void combine_residual_norm_kernel(const float* __restrict__ y,
-                                                                    const float* __restrict__ w, int H, int K,
-                                                                    float* __restrict__ x, float* __restrict__ layer_out,
-                                                                    float* __restrict__ xn) {
+// All slot rows of a column are loaded before the first fma, so a pass waits
+// for memory once. The updated row is kept in LDS with one pad float per 64 so
+// that the 64 chunk chains of the sum of squares read distinct banks.
+__global__ __launch_bounds__(1024) void combine_residual_norm_kernel(const float* __restrict__ y,
+                                                                     const float* __restrict__ w, int H, int K,
+                                                                     float* __restrict__ x,
+                                                                     float* __restrict__ layer_out,
+                                                                     float* __restrict__ xn) {
   extern __shared__ float row[];  // H + H/64 floats
   __shared__ float r_sh;
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const float* wt = w + (size_t)t * K;
+  const float* yt = y + (size_t)t * K * H;
   float* xr = x + (size_t)t * H;
-  for (int n = tid * 4; n < H; n += 1024) {
+  for (int n = tid * 4; n < H; n += nt * 4) {
+    v4f v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < K) v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(yt + (size_t)j * H + n));
+    float4 xv = *reinterpret_cast<const float4*>(xr + n);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < K; ++j) {
-      const float wj = wt[j];
-      const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * K + j) * H + n);
-      acc.x = __builtin_fmaf(wj, v.x, acc.x);
-      acc.y = __builtin_fmaf(wj, v.y, acc.y);
-      acc.z = __builtin_fmaf(wj, v.z, acc.z);
-      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < K) {
+        const float wj = wt[j];
+        acc.x = __builtin_fmaf(wj, v[j][0], acc.x);
+        acc.y = __builtin_fmaf(wj, v[j][1], acc.y);
+        acc.z = __builtin_fmaf(wj, v[j][2], acc.z);
+        acc.w = __builtin_fmaf(wj, v[j][3], acc.w);
+      }
     }
     if (layer_out) *reinterpret_cast<float4*>(layer_out + (size_t)t * H + n) = acc;
-    float4 xv = *reinterpret_cast<const float4*>(xr + n);
     xv.x = xv.x + acc.x;
     xv.y = xv.y + acc.y;
     xv.z = xv.z + acc.z;
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(256) void combine_residual_norm_kernel(const float*
   }
   __syncthreads();
   const float r = r_sh;
-  for (int n = tid; n < H; n += 256) xn[(size_t)t * H + n] = row[n + (n >> 6)] / r;
+  for (int n = tid; n < H; n += nt) xn[(size_t)t * H + n] = row[n + (n >> 6)] / r;
 }
 
 int grid_for(size_t n) {
@@ -145,6 +154,7 @@ hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, in
     if (e != hipSuccess) return e;
     lds_opt_in = true;
   }
-  combine_residual_norm_kernel<<<T, 256, lds, st>>>(y, w, H, K, x, layer_out, xn);
+  const int threads = H / 4 < 1024 ? H / 4 : 1024;  // H % 256 == 0: whole waves
+  combine_residual_norm_kernel<<<T, threads, lds, st>>>(y, w, H, K, x, layer_out, xn);
   return hipGetLastError();
 }

@@ -201,16 +201,14 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
 }
 
 // int8 requantization of the activation rows of the valid pairs: one
-// 256-thread workgroup per padded row, each thread holds I/256 values (loads
-// issued together), s = amax / 127, q = clamp(rint(a / s), +-127) stored as
-// FP8 hi/lo planes [2][I].
+// 256-thread workgroup per pair i (its row p = pos[i] in sort order), each
+// thread holds I/256 values (loads issued together), s = amax / 127,
+// q = clamp(rint(a / s), +-127) stored as FP8 hi/lo planes [2][I].
 __global__ __launch_bounds__(256) void requant_rows_kernel(const float* __restrict__ a, int I,
-                                                           const int32_t* __restrict__ sorted,
-                                                           const int32_t* __restrict__ n_rows, int P,
+                                                           const int32_t* __restrict__ pos,
                                                            uint8_t* __restrict__ aq8, float* __restrict__ as) {
   __shared__ float red[4];
-  const int p = blockIdx.x, tid = threadIdx.x;
-  if (p >= *n_rows || sorted[p] >= P) return;
+  const int p = pos[blockIdx.x], tid = threadIdx.x;
   const float* arow = a + (size_t)p * I;
   const int nu = I >> 10;  // four-element units per thread (I % 1024 == 0), else fallback below
   float v[4][4];
@@ -278,10 +276,10 @@ hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uin
   return hipGetLastError();
 }
 
-hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* sorted, const int32_t* n_rows, int max_rows, int P,
-                              uint8_t* aq8, float* as, hipStream_t st) {
-  if (max_rows <= 0) return hipSuccess;
-  requant_rows_kernel<<<max_rows, 256, 0, st>>>(a, I, sorted, n_rows, P, aq8, as);
+hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* pos, int P, uint8_t* aq8, float* as,
+                              hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  requant_rows_kernel<<<P, 256, 0, st>>>(a, I, pos, aq8, as);
   return hipGetLastError();
 }
 

@@ -71,6 +71,30 @@ __device__ __forceinline__ uint32_t pick_scales(uint32_t vx, uint32_t vy, int h)
   return (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi << 8) & 0xff000000u);
 }
 
+// The sort tile's pair-row scales (KD dwords a row) into LDS rows of KD + 1
+// dwords: eight loads in flight per thread before their stores.
+__device__ __forceinline__ void stage_row_scales(const uint8_t* __restrict__ act_scales, const int* lds_row, int rows,
+                                                 int KD, int KB, int nthreads, uint32_t* dst) {
+  const int total = rows * KD;
+  for (int i0 = threadIdx.x; i0 < total; i0 += 8 * nthreads) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * nthreads, ic = i < total ? i : 0;
+      const int r = ic / KD, d = ic - r * KD;
+      v[j] = reinterpret_cast<const uint32_t*>(act_scales + (size_t)lds_row[r] * KB)[d];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * nthreads;
+      if (i < total) {
+        const int r = i / KD, d = i - r * KD;
+        dst[r * (KD + 1) + d] = v[j];
+      }
+    }
+  }
+}
+
 template <bool GATE_UP>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act_codes,
@@ -128,10 +152,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     lds_pair[tid] = pr;
   }
   __syncthreads();
-  for (int i = tid; i < BM * KD; i += NWAVE * 64) {
-    const int r = i / KD, d = i - r * KD;
-    lds_s[r * (KD + 1) + d] = reinterpret_cast<const uint32_t*>(act_scales + (size_t)lds_row[r] * KB)[d];
-  }
+  stage_row_scales(act_scales, lds_row, BM, KD, KB, NWAVE * 64, lds_s);
 
   v16f acc[WTW][NU];
 #pragma unroll

@@ -42,8 +42,8 @@ int moe_k_decode_block_m();
 hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
                                 const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
                                 int max_tiles, int H, int I, int top_k, int P, float* a, hipStream_t st);
-hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* sorted, const int32_t* n_rows, int max_rows, int P,
-                              uint8_t* aq8, float* as, hipStream_t st);
+hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* pos, int P, uint8_t* aq8, float* as,
+                              hipStream_t st);
 hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
                              int H, int I, int top_k, int P, float* y, hipStream_t st);

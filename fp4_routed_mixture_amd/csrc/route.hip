@@ -18,17 +18,14 @@
 // desc, expert asc); w_j = s_j / S with S accumulated left to right in slot
 // order.
 //
-// Small batches keep the 64 chunk sums chunk-minor ([T][E][64]) so that the
-// finishing kernel reads each logit's sums as one 256-byte run.
-//
-// Small batches (T <= 64) keep all 64 chunk sums (one chunk per workgroup, so
-// each workgroup loads its operands once) and finish the whole tree in
+// Small batches (T <= 64) keep all 64 chunk sums, partial[64][T][E] (one
+// chunk per workgroup, so each workgroup loads its operands once, and writes
+// 64-byte runs of adjacent experts), and finish the whole tree in
 // topk_quant_token, one workgroup per token, which also quantizes the token's
 // row of x. Larger batches keep 8 slice sums; topk_quant uses one wave per
 // token.
 #include "common.h"
 #include "kernels.h"
-#include "sort_dev.h"
 
 namespace {
 
@@ -132,6 +129,12 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
           const float4 v = *reinterpret_cast<const float4*>(&xs[kk][ty * RA + a]);
           xa[a] = v.x; xa[a + 1] = v.y; xa[a + 2] = v.z; xa[a + 3] = v.w;
         }
+      } else if constexpr (RA % 2 == 0) {
+#pragma unroll
+        for (int a = 0; a < RA; a += 2) {
+          const float2 v = *reinterpret_cast<const float2*>(&xs[kk][ty * RA + a]);
+          xa[a] = v.x; xa[a + 1] = v.y;
+        }
       } else {
 #pragma unroll
         for (int a = 0; a < RA; ++a) xa[a] = xs[kk][ty * RA + a];
@@ -187,34 +190,22 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
     for (int b = 0; b < RB; ++b) {
       const int e = e0 + tx * RB + b;
       if (e < E) {
-        if (CPS == 1)
-          partial[((size_t)t * E + e) * 64 + slice] = st2[a][b];  // chunk-minor: one 256-byte run per logit
-        else
-          partial[((size_t)slice * T + t) * E + e] = st2[a][b];
+        partial[((size_t)slice * T + t) * E + e] = st2[a][b];
       }
     }
   }
 }
 
-// Logit of (t, e): the remaining tree levels over the NS slice sums (a
-// perfect pairwise tree in index order), then the bias. NS = 64 reads the
-// chunk-minor layout [T][E][64], NS = 8 the slice-major layout [8][T][E].
+// Logit of (t, e) from the NS slice sums of the slice-major layout
+// [NS][T][E] (NS = 8 or 64): the tree's remaining levels over the slices,
+// then the bias. A wave's load of one slice reads adjacent experts.
 template <int NS>
 __device__ __forceinline__ float finish_logit(const float* __restrict__ partial, const float* __restrict__ bias, int T,
                                               int E, int t, int e) {
   float v[NS];
-  if (NS == 64) {
-    const float4* p = reinterpret_cast<const float4*>(partial + ((size_t)t * E + e) * 64);
+  const size_t st = (size_t)T * E, o = (size_t)t * E + e;
 #pragma unroll
-    for (int i = 0; i < NS / 4; ++i) {
-      const float4 q = p[i];
-      v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-    }
-  } else {
-    const size_t st = (size_t)T * E, o = (size_t)t * E + e;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
-  }
+  for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
 #pragma unroll
   for (int w = NS; w > 1; w >>= 1)
 #pragma unroll
@@ -302,18 +293,19 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Top-k of one token's scores (sc[0..E), E <= 1024, scores >= 0) by one
+// Top-k of one token's scores (sc[0..E), E <= 64 NK, scores >= 0) by one
 // wave: K rounds of a wave argmax keyed (score desc, expert asc), the same
 // selection and slot order as a full sort. Lane l keeps experts l, l+64, ...
-// in registers as keys fp32 bits + 1 (scores are non-negative, so the bits
+// in NK registers as keys fp32 bits + 1 (scores are non-negative, so the bits
 // order like the values; 0 marks a taken or absent expert). A round is two
 // wave reductions: the largest key, then the lowest expert holding it.
 // Lane 0 writes slot j of sel_id / sel_s.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, int K, int* sel_id, float* sel_s) {
+template <int NK>
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ sc, int E, int K, int* sel_id, float* sel_s) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[16];
+  uint32_t key[NK];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NK; ++i) {
     const int e = lane + 64 * i;
     key[i] = e < E ? __float_as_uint(sc[e]) + 1u : 0u;
   }
@@ -322,7 +314,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, i
     uint32_t bk = key[0];
     int be = lane;
 #pragma unroll
-    for (int i = 1; i < 16; ++i)
+    for (int i = 1; i < NK; ++i)
       if (key[i] > bk) {  // strictly greater: the lower expert wins a tie
         bk = key[i];
         be = lane + 64 * i;
@@ -330,13 +322,22 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, i
     const uint32_t top = wave_umax(bk);
     const int e = (int)wave_umin(bk == top ? (uint32_t)be : 0xffffffffu);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NK; ++i)
       if (lane + 64 * i == e) key[i] = 0u;
     if (lane == 0) {
       sel_id[j] = e;
       sel_s[j] = __uint_as_float(top - 1u);
     }
   }
+}
+
+// The above with NK = the fewest registers that hold E experts (E <= 1024).
+__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int E, int K, int* sel_id, float* sel_s) {
+  if (E <= 64) wave_topk_n<1>(sc, E, K, sel_id, sel_s);
+  else if (E <= 128) wave_topk_n<2>(sc, E, K, sel_id, sel_s);
+  else if (E <= 256) wave_topk_n<4>(sc, E, K, sel_id, sel_s);
+  else if (E <= 512) wave_topk_n<8>(sc, E, K, sel_id, sel_s);
+  else wave_topk_n<16>(sc, E, K, sel_id, sel_s);
 }
 
 // Renormalized weights of the K selected scores: S accumulated left to right
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
 #pragma unroll 1
-  for (int e = lane; e < E; e += 64) sc[wave][e] = moe::sigmoid_fixed(finish_logit<8>(partial, bias, T, E, t, e));
+  for (int e = lane; e < E; e += 64) sc[wave][e] = moe::sigmoid_fixed(finish_logit<NSLICE>(partial, bias, T, E, t, e));
   // a wave reads only its own LDS rows: wave-level ordering suffices
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -469,6 +470,9 @@ hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, i
     if (T <= 16) {
       dim3 grid((E + 15) / 16, 1, 64);
       router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+    } else if (T <= 32) {
+      dim3 grid((E + 15) / 16, 1, 64);
+      router_partial_kernel<XT, 2, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
     } else {
       dim3 grid((E + 15) / 16, 1, 64);
       router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);

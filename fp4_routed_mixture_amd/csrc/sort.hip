@@ -4,11 +4,10 @@
 // expert segment padded to a multiple of block_m, plus the tile -> expert map
 // the grouped GEMMs walk. Integers only, so it is bit-exact by construction.
 //
-// Stability inside a wave comes from a match loop: the lanes holding the
-// lowest-numbered unprocessed expert vote (ballot), each learns its rank from
-// the popcount of the voting lanes below it, and they retire together. Waves
-// (and blocks) are ordered by pair index, so adding the counts of earlier
-// waves (blocks) keeps the global order stable.
+// Inside a block of up to 1024 pairs the stable rank of a pair is the number
+// of earlier pairs with its expert, read from a per-expert bitmask of the
+// block's pairs. Blocks are ordered by pair index, so adding the counts of
+// earlier blocks keeps the global order stable.
 //
 // Small P (<= 1024): one 1024-thread workgroup does everything.
 // Large P: sort_count (per 1024-pair block: stable local ranks + per-expert
@@ -28,14 +27,15 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ tile_expert,
                                                           int32_t* __restrict__ n_tiles) {
   extern __shared__ int smem[];
-  int* wcnt = smem;                  // 17 * E
-  int* offs = wcnt + 17 * E;         // E + 1
-  int* tmp = offs + E + 1;           // 1024
+  const int W = (P + 31) >> 5;
+  uint32_t* mask = reinterpret_cast<uint32_t*>(smem);  // E * W
+  int* tot = smem + E * W;                              // E
+  int* offs = tot + E;                                  // E + 1
+  int* tmp = offs + E + 1;                              // 1024
   const bool valid = (int)threadIdx.x < P;
   const int id = valid ? ids[threadIdx.x] : 0;
   int rank;
-  moe::block_rank(id, valid, E, wcnt, rank);
-  const int* tot = wcnt + 16 * E;
+  moe::block_rank(id, valid, P, E, mask, tot, rank);
   moe::scan_offsets(tot, E, block_m, offs, tmp);
   const int tid = threadIdx.x;
   if (valid) {
@@ -53,13 +53,16 @@ __global__ __launch_bounds__(1024) void sort_count_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ local_rank,
                                                           int32_t* __restrict__ block_hist) {
   extern __shared__ int smem[];
+  const int n = min(moe::SB, P - (int)blockIdx.x * moe::SB);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(smem);  // E * ceil(n / 32)
+  int* tot = smem + E * ((n + 31) >> 5);               // E
   const int i = blockIdx.x * moe::SB + threadIdx.x;
   const bool valid = i < P;
   const int id = valid ? ids[i] : 0;
   int rank;
-  moe::block_rank(id, valid, E, smem, rank);
+  moe::block_rank(id, valid, n, E, mask, tot, rank);
   if (valid) local_rank[i] = rank;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = smem[16 * E + e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) block_hist[(size_t)blockIdx.x * E + e] = tot[e];
 }
 
 // Large P, step 2: one workgroup. block_hist becomes per-block exclusive
@@ -158,14 +161,14 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
     lds_opt_in = true;
   }
   if (P <= moe::SB) {
-    size_t lds = (size_t)(17 * E + E + 1 + 1024) * 4;
+    size_t lds = (size_t)(E * ((P + 31) / 32) + E + E + 1 + 1024) * 4;
     sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles);
     return hipGetLastError();
   }
   int nb = (P + moe::SB - 1) / moe::SB;
   int32_t* local_rank = (int32_t*)scratch;
   int32_t* block_hist = (int32_t*)((char*)scratch + ((size_t)P * 4 + 255) / 256 * 256);
-  sort_count_kernel<<<nb, 1024, (size_t)17 * E * 4, st>>>(ids, P, E, local_rank, block_hist);
+  sort_count_kernel<<<nb, 1024, (size_t)(E * (moe::SB / 32) + E) * 4, st>>>(ids, P, E, local_rank, block_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scan_kernel<<<1, 1024, (size_t)(E + E + 1 + 1024) * 4, st>>>(nb, P, E, block_m, block_hist, counts, offsets,

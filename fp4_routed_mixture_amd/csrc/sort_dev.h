@@ -7,52 +7,34 @@ namespace moe {
 
 constexpr int SB = 1024;  // pairs per sort block (one 1024-thread workgroup)
 
-// Stable rank of each lane's id among lanes of this wave with the same id,
-// and (for the lane that is lowest in its group) the group size.
-__device__ __forceinline__ void wave_match_rank(int id, bool valid, int& rank, int& group_count, bool& leader) {
-  const int lane = threadIdx.x & 63;
-  uint64_t active = __ballot(valid);
-  rank = 0;
-  group_count = 0;
-  leader = false;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  while (active) {
-    int first = __ffsll((unsigned long long)active) - 1;
-    int fid = __shfl(id, first, 64);
-    uint64_t m = __ballot(valid && id == fid);
-    if (valid && id == fid) {
-      rank = __popcll(m & below);
-      group_count = __popcll(m);
-      leader = lane == first;
-    }
-    active &= ~m;
+// Per block of n <= SB pairs (thread i holds pair base + i, blockDim.x >= n):
+// stable local rank of each pair and the block's per-expert counts, from
+// bitmasks. Expert e owns W = ceil(n / 32) LDS words; bit i is set (an LDS
+// atomic OR: the result does not depend on the order of the ORs) when pair i
+// goes to e. The rank of pair i is the number of set bits below bit i in its
+// expert's words, the count of e the number of all its set bits.
+// mask: LDS [E][W] words; tot: LDS [E] (the block's totals on return).
+__device__ inline void block_rank(int my_id, bool my_valid, int n, int E, uint32_t* mask, int* tot, int& my_rank) {
+  const int tid = threadIdx.x;
+  const int W = (n + 31) >> 5;
+  for (int i = tid; i < E * W; i += blockDim.x) mask[i] = 0u;
+  __syncthreads();
+  if (my_valid) atomicOr(&mask[my_id * W + (tid >> 5)], 1u << (tid & 31));
+  __syncthreads();
+  my_rank = 0;
+  if (my_valid) {
+    const uint32_t* m = mask + my_id * W;
+    const int wi = tid >> 5;
+    int r = __popc(m[wi] & ((1u << (tid & 31)) - 1u));
+    for (int w = 0; w < wi; ++w) r += __popc(m[w]);
+    my_rank = r;
   }
-}
-
-// Per block of up to SB pairs (thread i holds pair base + i): stable local
-// rank of each pair and per-expert counts. wcnt: LDS [17][E]; row 16 receives
-// the block's per-expert totals.
-__device__ inline void block_rank(int my_id, bool my_valid, int E, int* wcnt, int& my_rank) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
-  __syncthreads();
-  int rank, cnt;
-  bool leader;
-  wave_match_rank(my_id, my_valid, rank, cnt, leader);
-  if (leader) wcnt[wave * E + my_id] = cnt;
-  __syncthreads();
-  // exclusive prefix over waves, per expert (in place), then local rank
   for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < 16; ++w) {
-      int c = wcnt[w * E + e];
-      wcnt[w * E + e] = run;
-      run += c;
-    }
-    wcnt[16 * E + e] = run;  // block total for e
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __popc(mask[e * W + w]);
+    tot[e] = c;
   }
   __syncthreads();
-  my_rank = my_valid ? wcnt[wave * E + my_id] + rank : 0;
 }
 
 // Block-wide exclusive scan of padded counts over E experts (E <= 1024,
@@ -85,13 +67,20 @@ __device__ inline void scan_offsets(const int* counts_lds, int E, int block_m, i
 }
 
 __device__ inline void write_tiles_and_padding(const int* counts, const int* offs, int E, int P, int block_m,
-                                        int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
-                                        int32_t* __restrict__ n_tiles) {
+                                               int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+                                               int32_t* __restrict__ n_tiles) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
-    for (int p = offs[e] + counts[e]; p < offs[e + 1]; ++p) sorted[p] = P;
-    for (int q = offs[e] / block_m; q < offs[e + 1] / block_m; ++q) tile_expert[q] = e;
+  // padding slots: (expert, slot) items spread over the threads, so the slots
+  // of one expert go to consecutive threads
+  if (block_m > 1) {
+    const int per = block_m - 1;
+    for (int i = tid; i < E * per; i += blockDim.x) {
+      const int e = i / per, p = offs[e] + counts[e] + (i - e * per);
+      if (p < offs[e + 1]) sorted[p] = P;
+    }
   }
+  for (int e = tid; e < E; e += blockDim.x)
+    for (int q = offs[e] / block_m; q < offs[e + 1] / block_m; ++q) tile_expert[q] = e;
   if (tid == 0) *n_tiles = offs[E] / block_m;
 }
 

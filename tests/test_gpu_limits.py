@@ -49,3 +49,26 @@ def test_shape_limits(name, T, H, I, E, k, act_mode):
         assert int((g["aq"] != o["aq"]).sum()) == 0
         assert_close_rms(g["out"], o["out"])
     del layer
+
+
+LARGE_EXPERT_CASES = [
+    # experts holding hundreds of rows: many full sort tiles per expert, ragged
+    # last tiles, one expert far heavier than the rest, and K = 4096 (the
+    # pair-row scales of a tile fill the most LDS)
+    ("two_experts", 300, 1024, 512, 2, 2),
+    ("ragged_heavy", 777, 2048, 1024, 8, 3),
+    ("k4096", 260, 4096, 2048, 2, 2),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k", LARGE_EXPERT_CASES)
+def test_large_experts(name, T, H, I, E, k):
+    w = S.Workload(name, T, H, I, E, k, S.X_BF16, S.ACT_MXFP4, False, 41)
+    print(f"[large-experts] {S.describe(w)}", flush=True)
+    layer = SD.load_layer(w)
+    g = run_forward(w, layer, SD.activations(w), taps=True)
+    o = oracle_layer(w, S.activations(w), intermediates=True)
+    assert np.array_equal(g["ids"], o["ids"])
+    assert int((g["aq"] != o["aq"]).sum()) == 0
+    assert_close_rms(g["out"], o["out"])
+    del layer
