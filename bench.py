@@ -71,6 +71,32 @@ def per_expert_bytes(w):
     return w13, w2
 
 
+def graph_time(fn, reps: int, torch, sleep_ms: float = 20.0) -> float:
+    """ms per replay of fn() captured into one HIP graph (after a warm-up call
+    on a side stream), replayed `reps` times back to back behind a bounded GPU
+    sleep."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(sleep_ms * 2.4e6))
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) / reps
+
+
 def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, ev: HipEvents,
                  sleep_ms: float = 20.0, sample_every: int = 4) -> dict:
     w = S.WORKLOADS[name]
@@ -140,6 +166,13 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
     for e in d_events:
         ev.destroy(e)
 
+    # the same steps from a HIP graph: one graph holds the `rot` layer calls of
+    # one rotation, replayed steps / rot times
+    def rotation():
+        for i in range(rot):
+            step(i)
+    graph_ms = graph_time(rotation, max(1, steps // rot), torch, sleep_ms) / rot
+
     # routing statistics of each rotated batch (its distinct experts set the bytes)
     distinct = []
     max_load = []
@@ -165,6 +198,7 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
         "gpu_bound": host_s < sleep_ms / 1e3, "gate_up_ms_min": float(np.min(g1_all)),
         "gate_up_samples": len(g1_all),
         "ms_per_step": ms_step, "tokens_per_s": T / (ms_step / 1e3),
+        "graph_ms_per_step": graph_ms, "graph_tokens_per_s": T / (graph_ms / 1e3),
         "stage_ms": stage_ms, "distinct_experts": d_avg, "max_load": max_load,
         "layer_alg_bytes": layer_bytes, "layer_hbm_gbs": layer_bytes / (ms_step / 1e3) / 1e9,
         "layer_fp4_tflops": layer_flops / (ms_step / 1e3) / 1e12,
@@ -199,6 +233,8 @@ def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: flo
     t_end.record()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / steps
+    # the same step (all layers) replayed from one HIP graph
+    graph_ms = graph_time(lambda: B.moe_forward_stack(cfg, x, layers, ws), steps, torch, sleep_ms)
 
     # routing of every layer on the first step's stream (diagnostic, untimed):
     # the distinct experts each layer reads set the algorithmic bytes
@@ -222,9 +258,10 @@ def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: flo
     del layers
     return {"workload": name, "layers": L, "T": T, "steps": steps, "ms_per_step": ms_step,
             "tokens_per_s": T / (ms_step / 1e3), "host_enqueue_ms": host_s * 1e3 / steps,
+            "graph_ms_per_step": graph_ms, "graph_tokens_per_s": T / (graph_ms / 1e3),
             "gpu_bound": host_s < sleep_ms / 1e3 + steps * ms_step / 1e3,
             "distinct_experts_per_layer": float(np.mean(distinct)), "step_alg_bytes": step_bytes,
-            "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9}
+            "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9, "graph_hbm_gbs": step_bytes / (graph_ms / 1e3) / 1e9}
 
 
 def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
@@ -310,8 +347,8 @@ def main():
     ev = HipEvents()
 
     main_res = run_workload(args.workload, args.steps, args.warmup, args.rot, torch, B, S, SD, ev)
-    print(f"# {args.workload}: {main_res['ms_per_step'] * 1e3:.1f} us/step, {main_res['tokens_per_s']:.0f} tok/s, "
-          f"stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in main_res["stage_ms"].items()),
+    print(f"# {args.workload}: {main_res['ms_per_step'] * 1e3:.1f} us/step, {main_res['tokens_per_s']:.0f} tok/s "
+          f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f} us/step), stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in main_res["stage_ms"].items()),
           file=sys.stderr, flush=True)
     legs = {}
     if not args.no_legs:
@@ -320,13 +357,14 @@ def main():
             torch.cuda.empty_cache()
             r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev)
             legs[name] = r
-            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['tokens_per_s']:.0f} tok/s, "
-                  f"layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
+            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step (graph {r['graph_ms_per_step'] * 1e3:.1f}), "
+                  f"{r['tokens_per_s']:.0f} tok/s, layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
                   + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         stack = run_stack("stack43_decode_t32", 5, 1, torch, B, S, SD)
         print(f"# stack43_decode_t32: {stack['ms_per_step']:.2f} ms/step (43 layers), {stack['tokens_per_s']:.0f} "
-              f"tok/s, {stack['hbm_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+              f"tok/s, {stack['hbm_gbs']:.0f} GB/s; graph {stack['graph_ms_per_step']:.2f} ms/step, "
+              f"{stack['graph_tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
 
     w = S.WORKLOADS[args.workload]
     mx = w.act_mode == S.ACT_MXFP4
@@ -361,9 +399,13 @@ def main():
                    "routing": "zipf1.1" if w.zipf else "uniform", "distinct_layers_cycled": args.rot},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "graph": {"ms_per_step": round(main_res["graph_ms_per_step"], 5),
+                  "tokens_per_s": round(main_res["graph_tokens_per_s"], 1)},
         "stage_us_diagnostic": {k: round(v * 1e3, 2) for k, v in main_res["stage_ms"].items()},
         "distinct_experts": main_res["distinct_experts"],
         "legs": {k: {"tokens_per_s": round(v["tokens_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
+                     "graph_tokens_per_s": round(v["graph_tokens_per_s"], 1),
+                     "graph_ms_per_step": round(v["graph_ms_per_step"], 5),
                      "layer_hbm_gbs": round(v["layer_hbm_gbs"], 1),
                      "layer_hbm_frac": round(v["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
                      "layer_fp4_tflops": round(v["layer_fp4_tflops"], 1),
@@ -377,6 +419,9 @@ def main():
             "tokens_per_s": round(stack["tokens_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
             "layers": stack["layers"], "hbm_gbs": round(stack["hbm_gbs"], 1),
             "hbm_frac": round(stack["hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "graph_tokens_per_s": round(stack["graph_tokens_per_s"], 1),
+            "graph_ms_per_step": round(stack["graph_ms_per_step"], 4),
+            "graph_hbm_frac": round(stack["graph_hbm_gbs"] / HBM_PEAK_GBS, 4),
             "distinct_experts_per_layer": stack["distinct_experts_per_layer"],
             "host_enqueue_ms_per_step": round(stack["host_enqueue_ms"], 3)}
     print(json.dumps(line))

@@ -267,7 +267,7 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
 
 
-  // route (+ for P <= 1024: top-k, sort and quantization of x in one kernel)
+  // route: partial logits, then top-k with the quantization of x
   MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
   MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, s));
   MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
