@@ -319,6 +319,8 @@ def main():
     ap.add_argument("--workload", default="decode_t4")
     ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
     ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
+    ap.add_argument("--legs", default="decode_t64_zipf,prefill_t4604_zipf,prefill_t16384_zipf,stack43_decode_t32",
+                    help="comma-separated legs to run after the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
@@ -351,15 +353,20 @@ def main():
           f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f} us/step), stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in main_res["stage_ms"].items()),
           file=sys.stderr, flush=True)
     legs = {}
-    if not args.no_legs:
+    want = set() if args.no_legs else set(args.legs.split(","))
+    stack = None
+    if want:
         for name, steps, rot in (("decode_t64_zipf", 32, 8), ("prefill_t4604_zipf", 10, 2),
                                  ("prefill_t16384_zipf", 4, 2)):
+            if name not in want:
+                continue
             torch.cuda.empty_cache()
             r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev)
             legs[name] = r
             print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step (graph {r['graph_ms_per_step'] * 1e3:.1f}), "
                   f"{r['tokens_per_s']:.0f} tok/s, layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
                   + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
+    if "stack43_decode_t32" in want:
         torch.cuda.empty_cache()
         stack = run_stack("stack43_decode_t32", 5, 1, torch, B, S, SD)
         print(f"# stack43_decode_t32: {stack['ms_per_step']:.2f} ms/step (43 layers), {stack['tokens_per_s']:.0f} "
@@ -414,7 +421,7 @@ def main():
                      "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
                      "distinct_experts": v["distinct_experts"]} for k, v in legs.items()},
     }
-    if not args.no_legs:
+    if stack is not None:
         line["legs"]["stack43_decode_t32"] = {
             "tokens_per_s": round(stack["tokens_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
             "layers": stack["layers"], "hbm_gbs": round(stack["hbm_gbs"], 1),
