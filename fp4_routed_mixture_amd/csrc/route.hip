@@ -61,12 +61,13 @@ __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return moe
 // are in flight while the current stage is computed.
 // ---------------------------------------------------------------------------
 template <typename XT, int RA, int RB, int KS, int CPS>
-__global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
+__global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
                                                              float* __restrict__ partial, int T, int H, int E) {
   static_assert(CPS == 1 || CPS == 8, "chunks per slice");
   constexpr int TT = 16 * RA, TE = 16 * RB;
   constexpr int NX = TT * KS / 4 / 256, NW = TE * KS / 4 / 256;  // float4 groups per thread
   static_assert(NX >= 1 && NW >= 1, "tile too small for the stage");
+  static_assert(KS % 4 == 0, "k groups of four");
   // rows padded to a 16-byte multiple: each thread reads its RA (RB) operands
   // of one k as 16-byte LDS loads, the 16 lanes of a row group contiguous
   __shared__ __attribute__((aligned(16))) float xs[KS][TT + 4];
@@ -120,65 +121,94 @@ __global__ __launch_bounds__(256) void router_partial_kernel(const XT* __restric
     stash();
     __syncthreads();
     if (k0 + KS < kend) fetch(k0 + KS);
-#pragma unroll 4
-    for (int kk = 0; kk < KS; ++kk) {
-      float xa[RA], wb[RB];
-      if constexpr (RA % 4 == 0) {
+    // Four k per group (L % 4 == 0, so a chunk never ends inside a group):
+    // the group's LDS reads are issued together, then its fmas run in
+    // ascending k per output. With one chunk per slice (small batches: L is a
+    // multiple of KS) a chunk can only end with a stage, so the stage runs
+    // branch-free and fully unrolled; otherwise the chunk end is checked after
+    // every group (unrolling the 8-chunk slices measured slower: the hoisted
+    // reads halve the occupancy).
+    auto group = [&](int kk) {
+      float xa[4][RA], wb[4][RB];
 #pragma unroll
-        for (int a = 0; a < RA; a += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(&xs[kk][ty * RA + a]);
-          xa[a] = v.x; xa[a + 1] = v.y; xa[a + 2] = v.z; xa[a + 3] = v.w;
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (RA % 4 == 0) {
+#pragma unroll
+          for (int a = 0; a < RA; a += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(&xs[kk + u][ty * RA + a]);
+            xa[u][a] = v.x; xa[u][a + 1] = v.y; xa[u][a + 2] = v.z; xa[u][a + 3] = v.w;
+          }
+        } else if constexpr (RA % 2 == 0) {
+#pragma unroll
+          for (int a = 0; a < RA; a += 2) {
+            const float2 v = *reinterpret_cast<const float2*>(&xs[kk + u][ty * RA + a]);
+            xa[u][a] = v.x; xa[u][a + 1] = v.y;
+          }
+        } else {
+#pragma unroll
+          for (int a = 0; a < RA; ++a) xa[u][a] = xs[kk + u][ty * RA + a];
         }
-      } else if constexpr (RA % 2 == 0) {
+        if constexpr (RB % 4 == 0) {
 #pragma unroll
-        for (int a = 0; a < RA; a += 2) {
-          const float2 v = *reinterpret_cast<const float2*>(&xs[kk][ty * RA + a]);
-          xa[a] = v.x; xa[a + 1] = v.y;
+          for (int b = 0; b < RB; b += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(&ws[kk + u][tx * RB + b]);
+            wb[u][b] = v.x; wb[u][b + 1] = v.y; wb[u][b + 2] = v.z; wb[u][b + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < RB; ++b) wb[u][b] = ws[kk + u][tx * RB + b];
         }
-      } else {
-#pragma unroll
-        for (int a = 0; a < RA; ++a) xa[a] = xs[kk][ty * RA + a];
       }
-      if constexpr (RB % 4 == 0) {
 #pragma unroll
-        for (int b = 0; b < RB; b += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(&ws[kk][tx * RB + b]);
-          wb[b] = v.x; wb[b + 1] = v.y; wb[b + 2] = v.z; wb[b + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < RB; ++b) wb[b] = ws[kk][tx * RB + b];
-      }
-#pragma unroll
-      for (int a = 0; a < RA; ++a)
-#pragma unroll
-        for (int b = 0; b < RB; ++b) acc[a][b] = __builtin_fmaf(xa[a], wb[b], acc[a][b]);
-      if (++in_chunk == L) {
-        in_chunk = 0;
-        // push the chunk sums: chunk index within the slice = 3-bit counter
-        const bool b0 = chunk & 1, b1 = chunk & 2, b2 = chunk & 4;
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int a = 0; a < RA; ++a)
 #pragma unroll
-          for (int b = 0; b < RB; ++b) {
-            float v = acc[a][b];
-            acc[a][b] = 0.f;
-            if (CPS == 1) {
-              st2[a][b] = v;  // the chunk sum itself (tree level 0)
-            } else if (!b0) {
-              st0[a][b] = v;
+          for (int b = 0; b < RB; ++b) acc[a][b] = __builtin_fmaf(xa[u][a], wb[u][b], acc[a][b]);
+    };
+    auto push = [&]() {
+      // push the chunk sums: chunk index within the slice = 3-bit counter
+      const bool b0 = chunk & 1, b1 = chunk & 2, b2 = chunk & 4;
+#pragma unroll
+      for (int a = 0; a < RA; ++a)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          float v = acc[a][b];
+          acc[a][b] = 0.f;
+          if (CPS == 1) {
+            st2[a][b] = v;  // the chunk sum itself (tree level 0)
+          } else if (!b0) {
+            st0[a][b] = v;
+          } else {
+            v = st0[a][b] + v;
+            if (!b1) {
+              st1[a][b] = v;
             } else {
-              v = st0[a][b] + v;
-              if (!b1) {
-                st1[a][b] = v;
-              } else {
-                v = st1[a][b] + v;
-                if (!b2) st2[a][b] = v;
-                else st2[a][b] = st2[a][b] + v;  // chunk 7: the slice total
-              }
+              v = st1[a][b] + v;
+              if (!b2) st2[a][b] = v;
+              else st2[a][b] = st2[a][b] + v;  // chunk 7: the slice total
             }
           }
-        ++chunk;
+        }
+      ++chunk;
+    };
+    if (CPS == 1 && L % KS == 0) {
+#pragma unroll
+      for (int kk = 0; kk < KS; kk += 4) group(kk);
+      in_chunk += KS;
+      if (in_chunk == L) {
+        in_chunk = 0;
+        push();
+      }
+    } else {
+#pragma unroll 1
+      for (int kk = 0; kk < KS; kk += 4) {
+        group(kk);
+        in_chunk += 4;
+        if (in_chunk == L) {
+          in_chunk = 0;
+          push();
+        }
       }
     }
   }
