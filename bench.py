@@ -319,7 +319,8 @@ def main():
     ap.add_argument("--workload", default="decode_t4")
     ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
     ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
-    ap.add_argument("--legs", default="decode_t64_zipf,prefill_t4604_zipf,prefill_t16384_zipf,stack43_decode_t32",
+    ap.add_argument("--legs", default="decode_t64_zipf,prefill_t4604_zipf,prefill_t16384_zipf,stack43_decode_t32,"
+                                      "decode_t4_tp4,prefill_t4604_zipf_tp4",
                     help="comma-separated legs to run after the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -357,7 +358,8 @@ def main():
     stack = None
     if want:
         for name, steps, rot in (("decode_t64_zipf", 32, 8), ("prefill_t4604_zipf", 10, 2),
-                                 ("prefill_t16384_zipf", 4, 2)):
+                                 ("prefill_t16384_zipf", 4, 2), ("decode_t4_tp4", 64, 8),
+                                 ("prefill_t4604_zipf_tp4", 10, 2)):
             if name not in want:
                 continue
             torch.cuda.empty_cache()

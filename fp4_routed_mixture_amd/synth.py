@@ -90,6 +90,10 @@ WORKLOADS = {
     "prefill_t4604_zipf": Workload("prefill_t4604_zipf", 4604, 4096, 2048, 256, 6, X_BF16, ACT_MXFP4, True, 3),
     "stack43_decode_t32": Workload("stack43_decode_t32", 32, 4096, 2048, 256, 6, X_F32, ACT_INT8, False, 4, 43),
     "prefill_t16384_zipf": Workload("prefill_t16384_zipf", 16384, 4096, 2048, 256, 6, X_BF16, ACT_MXFP4, True, 4),
+    # one GPU's share under tensor parallelism over I across 4 GPUs (I/4 of
+    # every expert, the router replicated), at the decode and 4,604-token shapes
+    "decode_t4_tp4": Workload("decode_t4_tp4", 4, 4096, 512, 256, 6, X_BF16, ACT_INT8, False, 1),
+    "prefill_t4604_zipf_tp4": Workload("prefill_t4604_zipf_tp4", 4604, 4096, 512, 256, 6, X_BF16, ACT_MXFP4, True, 3),
 }
 
 

@@ -58,7 +58,7 @@ def test_forward_tiny_with_intermediates(name):
         assert np.array_equal(g["out"], o["out"])
 
 
-@pytest.mark.parametrize("name", ["decode_t4", "decode_t64_zipf"])
+@pytest.mark.parametrize("name", ["decode_t4", "decode_t64_zipf", "decode_t4_tp4"])
 def test_forward_decode_full(name):
     w = S.WORKLOADS[name]
     print(f"[forward] {S.describe(w)}", flush=True)
@@ -85,7 +85,8 @@ def _sample_tokens(w, ids, n, seed=0):
     return np.array(sorted(pick))
 
 
-@pytest.mark.parametrize("name,n", [("prefill_t4604_zipf", 48), ("prefill_t16384_zipf", 24)])
+@pytest.mark.parametrize("name,n", [("prefill_t4604_zipf", 48), ("prefill_t16384_zipf", 24),
+                                    ("prefill_t4604_zipf_tp4", 32)])
 def test_forward_prefill_sampled(name, n):
     w = S.WORKLOADS[name]
     print(f"[forward] {S.describe(w)}", flush=True)
