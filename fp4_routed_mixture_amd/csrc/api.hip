@@ -38,6 +38,14 @@ int check_shape(const moe_config* c) {
   if (c->I < 128 || c->I > 16384 || c->I % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->E < 1 || c->E > 1024) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->E) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->act_mode == MOE_ACT_MXFP4) {
+    // the prefill GEMMs address activation rows with 32-bit byte offsets:
+    // tokens x H/2 (gate/up) and padded pair rows x I/2 (down) stay below 2^32
+    const uint64_t P = (uint64_t)c->T * c->top_k;
+    const uint64_t cap = P + (uint64_t)(c->E < (int64_t)P ? c->E : P) * 63;
+    if ((uint64_t)c->T * (c->H / 2) >= (1ull << 32) || cap * (c->I / 2) >= (1ull << 32))
+      return MOE_ERR_UNSUPPORTED_SHAPE;
+  }
   return MOE_OK;
 }
 

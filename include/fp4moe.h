@@ -57,8 +57,10 @@
  *   - Calls may run concurrently on different streams if they use different
  *     workspaces and outputs.
  *   - Shape limits: 1 <= T <= 1<<20, H % 256 == 0, 256 <= H <= 16384,
- *     I % 128 == 0, 128 <= I <= 16384, 1 <= E <= 1024, 1 <= top_k <= min(E, 16).
- *     T = 0 is accepted and does nothing.
+ *     I % 128 == 0, 128 <= I <= 16384, 1 <= E <= 1024, 1 <= top_k <= min(E, 16);
+ *     with MOE_ACT_MXFP4 also T * H/2 < 2^32 and
+ *     (T*top_k + min(E, T*top_k) * 63) * I/2 < 2^32 (the prefill GEMMs address
+ *     activation rows with 32-bit offsets). T = 0 is accepted and does nothing.
  *   - Alignment: weights, x, out, quantized buffers: 16 bytes.
  */
 #ifndef FP4MOE_H

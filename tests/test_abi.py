@@ -65,6 +65,12 @@ def test_workspace_size_and_shape_checks(L):
     assert ws_status(cfg(E=4, top_k=5))[0] == 2
     assert ws_status(cfg(x_dtype=3))[0] == 1
     assert ws_status(cfg(act_mode=2))[0] == 1
+    # MXFP4 rows are addressed with 32-bit offsets: T * H/2 and the padded
+    # pair rows * I/2 must stay below 2^32
+    assert ws_status(cfg(act_mode=1, T=1 << 19, H=16384, I=128, top_k=1))[0] == 2
+    assert ws_status(cfg(act_mode=1, T=(1 << 19) - 1, H=16384, I=128, top_k=1))[0] == 0
+    assert ws_status(cfg(act_mode=1, T=1 << 18, H=256, I=16384, top_k=2))[0] == 2
+    assert ws_status(cfg(act_mode=0, T=1 << 19, H=16384, I=128, top_k=1))[0] == 0
     assert L.moe_workspace_size(None, None) == 1
 
 
