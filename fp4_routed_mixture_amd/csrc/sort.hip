@@ -19,6 +19,8 @@
 
 namespace {
 
+constexpr size_t kScanLdsMax = 156 * 1024;  // dynamic LDS of the scan with the histogram staged
+
 
 // P <= moe::SB: everything in one workgroup.
 __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m,
@@ -66,7 +68,11 @@ __global__ __launch_bounds__(1024) void sort_count_kernel(const int32_t* __restr
 }
 
 // Large P, step 2: one workgroup. block_hist becomes per-block exclusive
-// bases (offset of the expert segment plus earlier blocks' counts).
+// bases (offset of the expert segment plus earlier blocks' counts). With
+// HIST_LDS the whole [nblocks][E] matrix is first copied into LDS (every
+// load in flight at once) and written back at the end; otherwise the runs
+// below walk it in global memory.
+template <bool HIST_LDS>
 __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int E, int block_m,
                                                          int32_t* __restrict__ block_hist,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -77,7 +83,26 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
   int* tot = smem;            // E
   int* offs = tot + E;        // E + 1
   int* tmp = offs + E + 1;    // 1024
+  int* lh = tmp + 1024;       // nblocks * E (HIST_LDS)
+  int32_t* hist = HIST_LDS ? lh : block_hist;
   const int tid = threadIdx.x;
+  const int nh = nblocks * E;
+  if (HIST_LDS) {
+    for (int i0 = tid; i0 < nh; i0 += 8 * 1024) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * 1024;
+        v[j] = i < nh ? block_hist[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j * 1024;
+        if (i < nh) lh[i] = v[j];
+      }
+    }
+    __syncthreads();
+  }
   // Per expert, an exclusive scan over the blocks. With E <= 256 each expert
   // gets 1024 / E' threads (E' = E rounded up to a power of two) that scan
   // contiguous runs of blocks, then add the sums of the runs before them.
@@ -89,7 +114,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
     const int b0 = (nblocks * r) / split, b1 = (nblocks * (r + 1)) / split;
     int run = 0;
     if (e < E)
-      for (int b = b0; b < b1; ++b) run += block_hist[(size_t)b * E + e];
+      for (int b = b0; b < b1; ++b) run += hist[(size_t)b * E + e];
     part[tid] = run;
     __syncthreads();
     int base = 0, total = 0;
@@ -105,8 +130,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
     if (e < E) {
       run = base;
       for (int b = b0; b < b1; ++b) {
-        const int c = block_hist[(size_t)b * E + e];
-        block_hist[(size_t)b * E + e] = run;
+        const int c = hist[(size_t)b * E + e];
+        hist[(size_t)b * E + e] = run;
         run += c;
       }
     }
@@ -118,8 +143,12 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
     const int b0 = (nblocks * r) / split, b1 = (nblocks * (r + 1)) / split;
     if (e < E) {
       if (r == 0) counts[e] = tot[e];
-      for (int b = b0; b < b1; ++b) block_hist[(size_t)b * E + e] += offs[e];
+      for (int b = b0; b < b1; ++b) hist[(size_t)b * E + e] += offs[e];
     }
+  }
+  if (HIST_LDS) {
+    __syncthreads();
+    for (int i = tid; i < nh; i += 1024) block_hist[i] = lh[i];
   }
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
@@ -156,8 +185,11 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     hipError_t e2 = hipFuncSetAttribute((const void*)sort_count_kernel,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e3 = hipFuncSetAttribute((const void*)sort_scan_kernel<true>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScanLdsMax);
     if (e1 != hipSuccess) return e1;
     if (e2 != hipSuccess) return e2;
+    if (e3 != hipSuccess) return e3;
     lds_opt_in = true;
   }
   if (P <= moe::SB) {
@@ -171,8 +203,13 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
   sort_count_kernel<<<nb, 1024, (size_t)(E * (moe::SB / 32) + E) * 4, st>>>(ids, P, E, local_rank, block_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  sort_scan_kernel<<<1, 1024, (size_t)(E + E + 1 + 1024) * 4, st>>>(nb, P, E, block_m, block_hist, counts, offsets,
-                                                                    sorted, tile_expert, n_tiles);
+  const size_t scan_lds = (size_t)(E + E + 1 + 1024) * 4, hist_lds = (size_t)nb * E * 4;
+  if (scan_lds + hist_lds <= kScanLdsMax)
+    sort_scan_kernel<true><<<1, 1024, scan_lds + hist_lds, st>>>(nb, P, E, block_m, block_hist, counts, offsets,
+                                                                 sorted, tile_expert, n_tiles);
+  else
+    sort_scan_kernel<false><<<1, 1024, scan_lds, st>>>(nb, P, E, block_m, block_hist, counts, offsets, sorted,
+                                                       tile_expert, n_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scatter_kernel<<<(P + 255) / 256, 256, 0, st>>>(ids, P, E, local_rank, block_hist, sorted, pos);
