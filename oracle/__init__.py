@@ -78,6 +78,10 @@ def lib():
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    f32p, i32p, f32p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.or_moe_layer_routed.restype = C.c_int
+        L.or_moe_layer_routed.argtypes = [C.c_void_p, C.c_void_p, i32p, f32p,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, f32p,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.or_rmsnorm.argtypes = [C.c_int, C.c_int, f32p, f32p]
         L.or_num_threads.restype = C.c_int
         L.or_set_num_threads.argtypes = [C.c_int]
@@ -223,20 +227,8 @@ def silu_mul(h):
 
 
 # ------------------------------------------------------------------ layer --
-def moe_layer(x, wr, bias, experts, top_k: int, act_mode: int, intermediates: bool = False) -> dict:
-    """The whole layer for the tokens in x.
-
-    experts: a sequence of length E whose entry e is None or a tuple
-    (w13 [2I,H/2], w13_scale [2I,H/32], w2 [H,I/2], w2_scale [H,I/32]) of
-    canonical uint8 arrays. act_mode 0 = int8 rows, 1 = MXFP4.
-    """
-    x = np.ascontiguousarray(x)
-    T, H = x.shape
-    x_dtype = 1 if x.dtype == np.uint16 else 0
-    if x_dtype == 0:
-        x = _f32(x)
-    wr = _f32(wr)
-    E = wr.shape[0]
+def _expert_pointers(experts, E):
+    """(ptr arrays, kept arrays, I) for the per-expert canonical weights."""
     I = None
     arrs = [[], [], [], []]
     keep = []
@@ -252,21 +244,45 @@ def moe_layer(x, wr, bias, experts, top_k: int, act_mode: int, intermediates: bo
         for a, v in zip(arrs, ex):
             a.append(v.ctypes.data_as(C.c_void_p).value)
     assert I is not None
-    ptr_arrays = [(C.c_void_p * E)(*a) for a in arrs]
+    return [(C.c_void_p * E)(*a) for a in arrs], keep, I
+
+
+def _intermediates(T, H, I, P, act_mode):
+    mx = act_mode == 1
+    return {
+        "xq": np.empty((T, H // 2), np.uint8) if mx else np.empty((T, H), np.int8),
+        "xs": np.empty((T, H // 32), np.uint8) if mx else np.empty(T, np.float32),
+        "h": np.empty((P, 2 * I), np.float32),
+        "aq": np.empty((P, I // 2), np.uint8) if mx else np.empty((P, I), np.int8),
+        "as": np.empty((P, I // 32), np.uint8) if mx else np.empty(P, np.float32),
+        "y": np.empty((P, H), np.float32),
+    }
+
+
+def _x_rows(x):
+    x = np.ascontiguousarray(x)
+    x_dtype = 1 if x.dtype == np.uint16 else 0
+    return (x if x_dtype else _f32(x)), x_dtype
+
+
+def moe_layer(x, wr, bias, experts, top_k: int, act_mode: int, intermediates: bool = False) -> dict:
+    """The whole layer for the tokens in x.
+
+    experts: a sequence of length E whose entry e is None or a tuple
+    (w13 [2I,H/2], w13_scale [2I,H/32], w2 [H,I/2], w2_scale [H,I/32]) of
+    canonical uint8 arrays. act_mode 0 = int8 rows, 1 = MXFP4.
+    """
+    x, x_dtype = _x_rows(x)
+    T, H = x.shape
+    wr = _f32(wr)
+    E = wr.shape[0]
+    ptr_arrays, keep, I = _expert_pointers(experts, E)
     cfg = _Cfg(T, H, I, E, top_k, x_dtype, act_mode)
     P = T * top_k
     out = np.empty((T, H), np.float32)
     ids = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
-    inter = {}
-    if intermediates:
-        mx = act_mode == 1
-        inter["xq"] = np.empty((T, H // 2), np.uint8) if mx else np.empty((T, H), np.int8)
-        inter["xs"] = np.empty((T, H // 32), np.uint8) if mx else np.empty(T, np.float32)
-        inter["h"] = np.empty((P, 2 * I), np.float32)
-        inter["aq"] = np.empty((P, I // 2), np.uint8) if mx else np.empty((P, I), np.int8)
-        inter["as"] = np.empty((P, I // 32), np.uint8) if mx else np.empty(P, np.float32)
-        inter["y"] = np.empty((P, H), np.float32)
+    inter = _intermediates(T, H, I, P, act_mode) if intermediates else {}
     b = None if bias is None else _f32(bias)
     rc = lib().or_moe_layer(C.byref(cfg), x.ctypes.data_as(C.c_void_p), wr, _ptr(b),
                             *[C.cast(p, C.c_void_p) for p in ptr_arrays], out, ids, w,
@@ -275,6 +291,31 @@ def moe_layer(x, wr, bias, experts, top_k: int, act_mode: int, intermediates: bo
         raise ValueError("oracle: a routed expert has no weights")
     del keep
     res = {"out": out, "ids": ids, "w": w}
+    res.update(inter)
+    return res
+
+
+def moe_layer_routed(x, ids, w, experts, act_mode: int, intermediates: bool = False) -> dict:
+    """The layer's expert part for routing given by the caller: ids [T][k]
+    (int32 in [0, E), E = len(experts)) and weights [T][k] (fp32); the same
+    steps after the routing as moe_layer."""
+    x, x_dtype = _x_rows(x)
+    T, H = x.shape
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = _f32(w)
+    k = ids.shape[1]
+    E = len(experts)
+    ptr_arrays, keep, I = _expert_pointers(experts, E)
+    cfg = _Cfg(T, H, I, E, k, x_dtype, act_mode)
+    out = np.empty((T, H), np.float32)
+    inter = _intermediates(T, H, I, T * k, act_mode) if intermediates else {}
+    rc = lib().or_moe_layer_routed(C.byref(cfg), x.ctypes.data_as(C.c_void_p), ids, w,
+                                   *[C.cast(p, C.c_void_p) for p in ptr_arrays], out,
+                                   *[_ptr(inter.get(n)) for n in ("xq", "xs", "h", "aq", "as", "y")])
+    if rc != 0:
+        raise ValueError("oracle: an id is out of range or its expert has no weights")
+    del keep
+    res = {"out": out}
     res.update(inter)
     return res
 

@@ -399,27 +399,20 @@ typedef struct {
  * t*k + j: ids/w [T][k]; xq (int8 [T][H] or codes [T][H/2]) and xs (fp32 [T]
  * or bytes [T][H/32]); h [P][2I]; aq/as like xq/xs with K = I; y [P][H].
  * Returns 0, or -1 if a needed expert pointer is NULL. */
-int or_moe_layer(const or_config* c, const void* x, const float* wr, const float* bias,
-                 const uint8_t* const* w13, const uint8_t* const* w13s,
-                 const uint8_t* const* w2, const uint8_t* const* w2s,
-                 float* out, int32_t* ids_out, float* w_out,
-                 void* xq_out, void* xs_out, float* h_out, void* aq_out, void* as_out, float* y_out)
+/* The layer's expert part for given routing: quantize x, per pair the
+ * gate/up row, SiLU-mul, requantization and the down row, then the combine.
+ * ids/wts [T][k] are the routing (ids in [0, E)); xf is x in fp32. */
+static int layer_given_routing(const or_config* c, const float* xf, const int32_t* ids, const float* wts,
+                               const uint8_t* const* w13, const uint8_t* const* w13s,
+                               const uint8_t* const* w2, const uint8_t* const* w2s, float* out,
+                               void* xq_out, void* xs_out, float* h_out, void* aq_out, void* as_out, float* y_out)
 {
-    const int T = c->T, H = c->H, I = c->I, E = c->E, k = c->top_k;
+    const int T = c->T, H = c->H, I = c->I, k = c->top_k;
     const int mx = c->act_mode == 1;
     const int P = T * k;
-    float* xf = (float*)malloc((size_t)T * H * sizeof(float));
-    float* logits = (float*)malloc((size_t)T * E * sizeof(float));
-    int32_t* ids = (int32_t*)malloc((size_t)P * sizeof(int32_t));
-    float* wts = (float*)malloc((size_t)P * sizeof(float));
-    or_x_to_f32(T, H, c->x_dtype, x, xf);
-    or_router_logits(T, H, E, xf, wr, bias, logits);
-    or_topk(T, E, k, logits, ids, wts, NULL);
     for (int p = 0; p < P; ++p)
-        if (!w13[ids[p]] || !w13s[ids[p]] || !w2[ids[p]] || !w2s[ids[p]]) {
-            free(xf); free(logits); free(ids); free(wts);
+        if (ids[p] < 0 || ids[p] >= c->E || !w13[ids[p]] || !w13s[ids[p]] || !w2[ids[p]] || !w2s[ids[p]])
             return -1;
-        }
 
     /* activation quantization of x (per token) */
     size_t xq_row = mx ? (size_t)H / 2 : (size_t)H;
@@ -470,11 +463,59 @@ int or_moe_layer(const or_config* c, const void* x, const float* wr, const float
             out[(size_t)t * H + n] = acc;
         }
 
-    if (ids_out) memcpy(ids_out, ids, (size_t)P * sizeof(int32_t));
-    if (w_out) memcpy(w_out, wts, (size_t)P * sizeof(float));
     if (y_out) memcpy(y_out, y, (size_t)P * H * sizeof(float));
-    free(xf); free(logits); free(ids); free(wts); free(xq); free(xs); free(y);
+    free(xq); free(xs); free(y);
     return 0;
+}
+
+/* Every output of the layer depends only on its own token, so the oracle
+ * computes any subset of tokens exactly as it would inside the whole batch.
+ * x: [T][H] (fp32 or bf16 bits) of the tokens to compute. Weights are given
+ * per expert (arrays of E pointers, canonical layout: W13 [2I][H/2] codes,
+ * [2I][H/32] scales; W2 [H][I/2], [H][I/32]); a NULL entry is allowed for an
+ * expert that no token selects. Optional outputs (NULL to skip), pair p =
+ * t*k + j: ids/w [T][k]; xq (int8 [T][H] or codes [T][H/2]) and xs (fp32 [T]
+ * or bytes [T][H/32]); h [P][2I]; aq/as like xq/xs with K = I; y [P][H].
+ * Returns 0, or -1 if a needed expert pointer is NULL. */
+int or_moe_layer(const or_config* c, const void* x, const float* wr, const float* bias,
+                 const uint8_t* const* w13, const uint8_t* const* w13s,
+                 const uint8_t* const* w2, const uint8_t* const* w2s,
+                 float* out, int32_t* ids_out, float* w_out,
+                 void* xq_out, void* xs_out, float* h_out, void* aq_out, void* as_out, float* y_out)
+{
+    const int T = c->T, H = c->H, E = c->E, k = c->top_k;
+    const int P = T * k;
+    float* xf = (float*)malloc((size_t)T * H * sizeof(float));
+    float* logits = (float*)malloc((size_t)T * E * sizeof(float));
+    int32_t* ids = (int32_t*)malloc((size_t)P * sizeof(int32_t));
+    float* wts = (float*)malloc((size_t)P * sizeof(float));
+    or_x_to_f32(T, H, c->x_dtype, x, xf);
+    or_router_logits(T, H, E, xf, wr, bias, logits);
+    or_topk(T, E, k, logits, ids, wts, NULL);
+    const int r = layer_given_routing(c, xf, ids, wts, w13, w13s, w2, w2s, out, xq_out, xs_out, h_out, aq_out,
+                                      as_out, y_out);
+    if (r == 0 && ids_out) memcpy(ids_out, ids, (size_t)P * sizeof(int32_t));
+    if (r == 0 && w_out) memcpy(w_out, wts, (size_t)P * sizeof(float));
+    free(xf); free(logits); free(ids); free(wts);
+    return r;
+}
+
+/* The layer without its router: the expert part for routing given by the
+ * caller (ids [T][k] in [0, E), weights [T][k]), as a rank of an
+ * expert-parallel deployment computes its dispatched pairs. Same outputs as
+ * or_moe_layer after the routing. Returns 0, or -1 for an id out of range or
+ * a NULL expert pointer it needs. */
+int or_moe_layer_routed(const or_config* c, const void* x, const int32_t* ids, const float* wts,
+                        const uint8_t* const* w13, const uint8_t* const* w13s,
+                        const uint8_t* const* w2, const uint8_t* const* w2s, float* out,
+                        void* xq_out, void* xs_out, float* h_out, void* aq_out, void* as_out, float* y_out)
+{
+    float* xf = (float*)malloc((size_t)c->T * c->H * sizeof(float));
+    or_x_to_f32(c->T, c->H, c->x_dtype, x, xf);
+    const int r = layer_given_routing(c, xf, ids, wts, w13, w13s, w2, w2s, out, xq_out, xs_out, h_out, aq_out,
+                                      as_out, y_out);
+    free(xf);
+    return r;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -181,3 +181,39 @@ def test_rmsnorm_within_bound(oracle):
     x64 = x.astype(np.float64)
     ref = x64 / np.sqrt(np.mean(x64 ** 2, axis=1, keepdims=True) + 1e-6)
     assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-7)
+
+
+@pytest.mark.parametrize("act_mode", [0, 1])
+def test_routed_layer_reproduces_the_routed_part(oracle, act_mode):
+    """Given the router's own routing, the router-free layer is the layer."""
+    w = TINY
+    ex = _experts(w)
+    x, wr = S.activations(w, T=9), S.router_weights(w)
+    full = oracle.moe_layer(x, wr, None, ex, 2, act_mode, intermediates=True)
+    r = oracle.moe_layer_routed(x, full["ids"], full["w"], ex, act_mode, intermediates=True)
+    for n in ("out", "xq", "xs", "h", "aq", "as", "y"):
+        assert np.array_equal(r[n], full[n]), n
+
+
+@pytest.mark.parametrize("act_mode", [0, 1])
+def test_routed_layer_one_row_per_pair(oracle, act_mode):
+    """Each (token, slot) pair as its own row with k = 1, as an expert-parallel
+    rank receives them: row p's output is fl32(w_p * y_p) with y_p the pair's
+    down-projection in the whole layer."""
+    w = TINY
+    ex = _experts(w)
+    x, wr = S.activations(w, T=5), S.router_weights(w)
+    full = oracle.moe_layer(x, wr, None, ex, 2, act_mode, intermediates=True)
+    rows = np.repeat(x, 2, axis=0)  # pair p = t*k + j reads token t
+    r = oracle.moe_layer_routed(rows, full["ids"].reshape(-1, 1), full["w"].reshape(-1, 1), ex, act_mode)
+    want = (full["w"].reshape(-1, 1).astype(np.float32) * full["y"]).astype(np.float32)
+    assert np.array_equal(r["out"], want)
+
+
+def test_routed_layer_rejects_bad_ids(oracle):
+    w = TINY
+    ex = _experts(w)
+    x = S.activations(w, T=2)
+    ids = np.array([[0, 1], [2, w.E]], np.int32)
+    with pytest.raises(ValueError):
+        oracle.moe_layer_routed(x, ids, np.full((2, 2), 0.5, np.float32), ex, 0)
