@@ -264,6 +264,59 @@ def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: flo
             "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9, "graph_hbm_gbs": step_bytes / (graph_ms / 1e3) / 1e9}
 
 
+def run_ep_rank(name: str, ranks: int, steps: int, warmup: int, torch, B, S, SD, sleep_ms: float = 20.0) -> dict:
+    """One rank's share under expert parallelism over `ranks` GPUs: the batch
+    is routed over all experts (the router replicated), experts are placed in
+    contiguous blocks of E/ranks, and the heaviest rank computes the pairs
+    routed to its block -- one row per pair, top_k = 1, its slice of the
+    weights -- through moe_forward_routed. The dispatch and return exchanges
+    are not part of it. A step is one such call."""
+    w = S.WORKLOADS[name]
+    lay = SD.load_layer(w)
+    cfg = SD.config(w)
+    x = SD.activations(w)
+    ids = torch.empty((w.T, w.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.top_k), dtype=torch.float32, device="cuda")
+    B.moe_route(cfg, x, lay["router_w"], lay["bias"], ids, wts, SD.workspace(cfg))
+    ids_h, w_h = ids.cpu().numpy().ravel(), wts.cpu().numpy().ravel()
+    per = w.E // ranks
+    load = np.bincount(ids_h // per, minlength=ranks)
+    r = int(np.argmax(load))
+    pairs = np.nonzero(ids_h // per == r)[0]
+    tok = torch.from_numpy(pairs // w.top_k).cuda()
+    x_rows = x[tok].contiguous()
+    ids_l = torch.from_numpy((ids_h[pairs] - per * r).astype(np.int32).reshape(-1, 1)).cuda()
+    w_l = torch.from_numpy(w_h[pairs].astype(np.float32).reshape(-1, 1)).cuda()
+    local = {n: lay[n].view(w.E, -1)[per * r:per * (r + 1)].contiguous() for n in ("w13", "w13s", "w2", "w2s")}
+    del lay
+    Pl = len(pairs)
+    lcfg = B.make_config(Pl, w.H, w.I, per, 1, w.x_dtype, w.act_mode)
+    ws = SD.workspace(lcfg)
+    out = torch.empty((Pl, w.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.moe_forward_routed(lcfg, x_rows, ids_l, w_l, local["w13"], local["w13s"], local["w2"], local["w2s"], out,
+                             ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(sleep_ms * 2.4e6))
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    b13, b2 = per_expert_bytes(w)
+    flops = 2.0 * Pl * (w.H * 2 * w.I + w.I * w.H)
+    used = len(np.unique(ids_h[pairs]))
+    return {"workload": f"{name} on rank {r} of {ranks} (experts {per * r}..{per * (r + 1) - 1})", "pairs": Pl,
+            "pair_share": Pl / len(ids_h), "experts_used": used, "ms_per_step": ms,
+            "pairs_per_s": Pl / (ms / 1e3), "fp4_tflops": flops / (ms / 1e3) / 1e12,
+            "hbm_gbs": used * (b13 + b2) / (ms / 1e3) / 1e9}
+
+
 def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
     """The oracle, untuned, on the host cores: whole layers of the same
     workload (rotating the same seeded batches) until about budget_s of CPU
@@ -320,7 +373,7 @@ def main():
     ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
     ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
     ap.add_argument("--legs", default="decode_t64_zipf,prefill_t4604_zipf,prefill_t16384_zipf,stack43_decode_t32,"
-                                      "decode_t4_tp4,prefill_t4604_zipf_tp4",
+                                      "decode_t4_tp4,prefill_t4604_zipf_tp4,prefill_t4604_zipf_ep8",
                     help="comma-separated legs to run after the headline workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -368,6 +421,13 @@ def main():
             print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step (graph {r['graph_ms_per_step'] * 1e3:.1f}), "
                   f"{r['tokens_per_s']:.0f} tok/s, layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
                   + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
+    ep = None
+    if "prefill_t4604_zipf_ep8" in want:
+        torch.cuda.empty_cache()
+        ep = run_ep_rank("prefill_t4604_zipf", 8, 10, 2, torch, B, S, SD)
+        print(f"# prefill_t4604_zipf_ep8: {ep['ms_per_step'] * 1e3:.1f} us/step, {ep['pairs']} pairs "
+              f"({100 * ep['pair_share']:.1f}% of all), {ep['fp4_tflops']:.0f} TF/s, {ep['hbm_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
     if "stack43_decode_t32" in want:
         torch.cuda.empty_cache()
         stack = run_stack("stack43_decode_t32", 5, 1, torch, B, S, SD)
@@ -423,6 +483,12 @@ def main():
                      "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
                      "distinct_experts": v["distinct_experts"]} for k, v in legs.items()},
     }
+    if ep is not None:
+        line["legs"]["prefill_t4604_zipf_ep8"] = {
+            "workload": ep["workload"], "pairs": ep["pairs"], "pair_share": round(ep["pair_share"], 4),
+            "experts_used": ep["experts_used"], "ms_per_step": round(ep["ms_per_step"], 5),
+            "pairs_per_s": round(ep["pairs_per_s"], 1), "fp4_tflops": round(ep["fp4_tflops"], 1),
+            "fp4_frac": round(ep["fp4_tflops"] / FP4_PEAK_TFLOPS, 4), "hbm_gbs": round(ep["hbm_gbs"], 1)}
     if stack is not None:
         line["legs"]["stack43_decode_t32"] = {
             "tokens_per_s": round(stack["tokens_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),

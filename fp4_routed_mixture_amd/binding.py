@@ -25,8 +25,8 @@ STAGES = ["router", "topk", "quant_x", "sort", "gate_up", "requant", "down", "co
 # every function that include/fp4moe.h declares
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_workspace_size",
            "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_sort", "moe_quantize",
-           "moe_forward", "moe_forward_taps", "moe_rmsnorm", "moe_residual_add", "moe_stack_workspace_size",
-           "moe_forward_stack"]
+           "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
+           "moe_stack_workspace_size", "moe_forward_stack"]
 
 
 class MoEError(RuntimeError):
@@ -79,6 +79,8 @@ def lib():
             "moe_forward": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_forward_taps": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            C.POINTER(moe_taps), vp, sz, vp]),
+            "moe_forward_routed": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, C.POINTER(moe_taps), vp, sz,
+                                             vp]),
             "moe_rmsnorm": (C.c_int, [i32, i32, vp, vp, vp]),
             "moe_residual_add": (C.c_int, [i64, vp, vp, vp]),
             "moe_stack_workspace_size": (C.c_int, [cfgp, C.POINTER(sz)]),
@@ -192,6 +194,24 @@ def moe_forward_taps(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale
     _check(lib().moe_forward_taps(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(w13), _p(w13_scale),
                                   _p(w2), _p(w2_scale), _p(out), _p(topk_ids_out), _p(topk_w_out), C.byref(t),
                                   _p(workspace), workspace.numel(), _s(stream)), "moe_forward_taps")
+    return bm.value
+
+
+def moe_forward_routed(cfg, x, topk_ids, topk_w, w13, w13_scale, w2, w2_scale, out, workspace, taps=None,
+                       stream=None):
+    """The layer without its router: routing given as topk_ids [T][k] int32
+    (in [0, E)) and topk_w [T][k] fp32 device tensors. taps as in
+    moe_forward_taps (returns the block size the kernels used)."""
+    bm = C.c_int32(0)
+    tp = None
+    if taps is not None:
+        ev = taps.get("events")
+        tp = moe_taps(*(_p(taps.get(n)) for n in ("xq", "xs", "aq", "as", "y", "counts", "offsets",
+                                                   "sorted_pairs", "pair_pos")),
+                      C.cast(C.pointer(bm), C.c_void_p), None if ev is None else C.cast(ev, C.c_void_p))
+    _check(lib().moe_forward_routed(C.byref(cfg), _p(x), _p(topk_ids), _p(topk_w), _p(w13), _p(w13_scale), _p(w2),
+                                    _p(w2_scale), _p(out), None if tp is None else C.byref(tp), _p(workspace),
+                                    workspace.numel(), _s(stream)), "moe_forward_routed")
     return bm.value
 
 

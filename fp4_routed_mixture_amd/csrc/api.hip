@@ -219,7 +219,8 @@ namespace {
 int forward_impl(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                  const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
                  int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
-                 size_t workspace_bytes, void* stream, bool combine);
+                 size_t workspace_bytes, void* stream, bool combine, const int32_t* given_ids = nullptr,
+                 const float* given_w = nullptr);
 }  // namespace
 
 int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
@@ -236,13 +237,16 @@ namespace {
 int forward_impl(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                  const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale, float* out,
                  int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps, void* workspace,
-                 size_t workspace_bytes, void* stream, bool combine) {
+                 size_t workspace_bytes, void* stream, bool combine, const int32_t* given_ids,
+                 const float* given_w) {
   int st = check_shape(cfg);
   if (st) return st;
   if (cfg->T == 0) return MOE_OK;
-  if (!x || !router_w || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w13_scale) || !aligned16(w2) ||
-      !aligned16(w2_scale) || !aligned16(out) || ((uintptr_t)workspace & 255))
+  const bool routed = given_ids != nullptr;
+  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace) return MOE_ERR_INVALID_ARG;
+  if (routed ? !given_w : !router_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || (!routed && !aligned16(router_w)) || !aligned16(w13) || !aligned16(w13_scale) ||
+      !aligned16(w2) || !aligned16(w2_scale) || !aligned16(out) || ((uintptr_t)workspace & 255))
     return MOE_ERR_ALIGNMENT;
   const int T = cfg->T, H = cfg->H, I = cfg->I, E = cfg->E, k = cfg->top_k;
   const bool mx = cfg->act_mode == MOE_ACT_MXFP4;
@@ -255,8 +259,8 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
 
   hipStream_t s = (hipStream_t)stream;
   float* logits = at<float>(workspace, p.logits);
-  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, p.ids);
-  float* w = topk_w_out ? topk_w_out : at<float>(workspace, p.w);
+  int32_t* ids = topk_ids_out && !routed ? topk_ids_out : at<int32_t>(workspace, p.ids);
+  float* w = topk_w_out && !routed ? topk_w_out : at<float>(workspace, p.w);
   uint8_t* xq = at<uint8_t>(workspace, p.xq);
   void* xs = at<void>(workspace, p.xs);
   int32_t* counts = at<int32_t>(workspace, p.counts);
@@ -275,15 +279,31 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
 
 
-  // route: partial logits, then top-k with the quantization of x
-  MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
-  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, s));
-  MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_TOPK));
-  MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, 1, mx, ids, w, xq, (uint8_t*)xs, s));
-  MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
-  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
-  MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
+  if (!routed) {
+    // route: partial logits, then top-k with the quantization of x
+    MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
+    MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, s));
+    MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_TOPK));
+    MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, 1, mx, ids, w, xq, (uint8_t*)xs, s));
+    MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
+    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
+  } else {
+    // the caller's routing (ids clamped into [0, E) so that no id addresses
+    // memory outside the per-expert arrays), then the quantization of x
+    MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
+    MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_TOPK));
+    MOE_TRY(moe_k_copy_routing(given_ids, given_w, P, E, ids, w, s));
+    MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
+    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));
+    if (mx)
+      MOE_TRY(moe_k_quant_mxfp4(cfg->x_dtype, x, T, H, xq, (uint8_t*)xs, s));
+    else
+      MOE_TRY(moe_k_quant_int8(cfg->x_dtype, x, T, H, 1, xq, (float*)xs, nullptr, 0, nullptr, s));
+    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
+  }
   // sort
   MOE_TRY(mark(2 * MOE_STAGE_SORT));
   MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
@@ -356,6 +376,14 @@ int moe_forward(const moe_config* cfg, const void* x, const float* router_w, con
                 int32_t* topk_ids_out, float* topk_w_out, void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_taps(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
                           nullptr, workspace, workspace_bytes, stream);
+}
+
+int moe_forward_routed(const moe_config* cfg, const void* x, const int32_t* topk_ids, const float* topk_w,
+                       const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       float* out, const moe_taps* taps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (cfg && cfg->T > 0 && (!topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, x, nullptr, nullptr, w13, w13_scale, w2, w2_scale, out, nullptr, nullptr, taps, workspace,
+                      workspace_bytes, stream, true, topk_ids, topk_w);
 }
 
 int moe_stack_workspace_size(const moe_config* cfg, size_t* bytes) {

@@ -27,6 +27,9 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
                       hipStream_t st);
 
+hipError_t moe_k_copy_routing(const int32_t* ids_in, const float* w_in, int P, int E, int32_t* ids, float* w,
+                              hipStream_t st);
+
 // quant.hip
 hipError_t moe_k_quant_int8(int in_dtype, const void* v, int rows, int K, int out_fp8pair, void* q, float* scales,
                             const int32_t* sorted, int P, const int32_t* n_rows, hipStream_t st);

@@ -154,6 +154,17 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
 }
 
+// Routing given by a caller: ids clamped into [0, E), weights copied.
+__global__ __launch_bounds__(256) void copy_routing_kernel(const int32_t* __restrict__ ids_in,
+                                                           const float* __restrict__ w_in, int P, int E,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P) return;
+  const int e = ids_in[i];
+  ids[i] = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  w[i] = w_in[i];
+}
+
 // Large P, step 3: scatter.
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                            const int32_t* __restrict__ local_rank,
@@ -168,6 +179,13 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 }
 
 }  // namespace
+
+hipError_t moe_k_copy_routing(const int32_t* ids_in, const float* w_in, int P, int E, int32_t* ids, float* w,
+                              hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  copy_routing_kernel<<<(P + 255) / 256, 256, 0, st>>>(ids_in, w_in, P, E, ids, w);
+  return hipGetLastError();
+}
 
 size_t moe_k_sort_scratch_bytes(int P, int E) {
   if (P <= moe::SB) return 0;

@@ -245,6 +245,23 @@ int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w
                      float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer without its router: the expert part of moe_forward (quantization
+ * of x, sort, gate/up + SiLU-mul + requantization, down, combine) for routing
+ * given by the caller -- as a rank of an expert-parallel deployment computes
+ * the (token, expert) pairs dispatched to it, for instance one row per pair
+ * with top_k = 1 and E = the rank's experts. The steps after the routing are
+ * those of moe_forward (gfx90a paper, abstract: FP4 routed experts), so with
+ * the router's own ids and weights the output equals moe_forward's bit for bit.
+ *   topk_ids int32 [T][top_k]: expert of each slot, in [0, E); an id outside
+ *     that range is clamped into it (memory-safe, result unspecified);
+ *   topk_w fp32 [T][top_k]: the slot weights of the combine;
+ *   router_w is not used; the other arguments and the workspace
+ *   (moe_workspace_size(cfg) bytes) are as for moe_forward; taps as for
+ *   moe_forward_taps (NULL for none). */
+int moe_forward_routed(const moe_config* cfg, const void* x, const int32_t* topk_ids, const float* topk_w,
+                       const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                       float* out, const moe_taps* taps, void* workspace, size_t workspace_bytes, void* stream);
+
 /* --------------------------------------------------- stacked-layer helpers --
  * Residual stream between stacked MoE layers, x_{l+1} = x_l + moe_l(rmsnorm(x_l)):
  * moe_rmsnorm: out[t] = x[t] / sqrt(ss / H + 1e-6), ss = the router's fixed-

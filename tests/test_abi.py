@@ -107,6 +107,19 @@ def test_forward_argument_errors(L):
     assert fwd(cfg(T=0), x=None, out=None) == 0  # empty batch: nothing to do
 
 
+def test_routed_forward_errors(L):
+    c = cfg()
+    f = L.moe_forward_routed
+    args = lambda ids=FAKE, w=FAKE, x=FAKE: (C.byref(c), x, ids, w, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 30), None,
+                                             FAKE + (1 << 34), 1 << 40, None)
+    assert f(*args(ids=None)) == 1
+    assert f(*args(w=None)) == 1
+    assert f(*args(x=None)) == 1
+    assert f(*args(x=FAKE + 8)) == 3
+    c0 = cfg(T=0)
+    assert f(C.byref(c0), None, None, None, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None) == 0
+
+
 def test_other_entry_point_errors(L):
     c = cfg()
     vp = C.c_void_p
