@@ -58,7 +58,9 @@ __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return moe
 // ---------------------------------------------------------------------------
 // Partial logits over one H slice. 256 threads = 16 x 16; tile (16 RA) tokens
 // x (16 RB) experts; KS k values per LDS stage; the next stage's global loads
-// are in flight while the current stage is computed.
+// are in flight while the current stage is computed. Four waves a SIMD (at
+// most 128 registers): the 16-output tile of large batches measured faster so
+// than with three waves and no spill.
 // ---------------------------------------------------------------------------
 template <typename XT, int RA, int RB, int KS, int CPS>
 __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
