@@ -17,9 +17,11 @@
 // straight into the MFMA operand registers: the prepacked layout stores each
 // 64-K step of a tile as 64 lanes x 16 bytes, one fully coalesced load per
 // tile and K-step, kept PF K-steps ahead in a register ring. The gathered pair
-// rows are shared by the 4 waves and go through LDS: each stage (128 K) is
-// loaded into registers two stages ahead, transposed into the operand layout
-// on its LDS store, and double-buffered.
+// rows are shared by the 4 waves and go through LDS: the two 128-K stages of
+// the next 4-step group are loaded into registers one group ahead and
+// transposed into the operand layout on their LDS store, into a 4-stage ring,
+// so that a group needs one barrier (the two barriers of a double buffer per
+// group measured about 1% slower).
 //
 // Scale dwords (four K-steps each) are loaded one group ahead; the MFMA's
 // byte select picks the K-step. The main loop has no branch between a load
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     int rows_are_tokens, uint8_t* __restrict__ aq, uint8_t* __restrict__ as, float* __restrict__ y, int out_n) {
   constexpr int S = GATE_UP ? 2 : 1;           // 32-row tiles per NT unit (gate/up pair or one W2 tile)
   constexpr int UPW = WTW / S;                 // NT units per wave
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[4][B_STAGE];
   extern __shared__ uint32_t lds_s[];  // pair-row scales (BM x (K/128 + 1) dwords), later the y staging
   __shared__ int lds_row[BM];
   __shared__ int lds_pair[BM];
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     for (int u = 0; u < NU; ++u) acc[t][u] = (v16f){};
 
   v4i ra[PF][WTW];      // weight ring: slot kt % PF
-  v4i rb[2][NBL];       // pair-row staging, set = stage & 1
+  v4i rb[2][NBL];       // pair-row staging of the next group, set = its stage
   uint32_t sa[WTW], sx[NU], sy[NU], na[WTW], nx[NU], ny[NU];
 
   auto aload = [&](int slot, int kt) {
@@ -233,13 +235,14 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     }
   };
 
-  // prologue: K-steps 0..PF-1, pair-row stages 0 (stored) and 1, then
-  // scale group 0 (the barrier also publishes the staged pair-row scales)
+  // prologue: K-steps 0..PF-1, pair-row stages 0 and 1 (group 0) stored,
+  // then scale group 0 (the barrier also publishes the staged pair-row scales)
 #pragma unroll
   for (int j = 0; j < PF; ++j) aload(j, j);
   bload(0, 0);
   bload(1, 1);
   bstore(0, 0);
+  bstore(1, 1);
   __syncthreads();
   load_scales(sa, sx, sy, 0);
   // group g = K-steps 4g..4g+3 = stages 2g (buffer 0) and 2g+1 (buffer 1);
@@ -248,22 +251,23 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   using I2 = std::integral_constant<int, 2>;
   using J2 = std::integral_constant<int, 2 % PF>;
   const int NG2 = NS >> 1;  // full groups
+  // group g reads buffers 2(g&1), 2(g&1)+1 and writes the next group's two
+  // stages into the other pair, read last in group g-1 (before the barrier
+  // that ended it): one barrier per group
   for (int g = 0; g < NG2; ++g) {
-    const int st = 2 * g;
+    const int st = 2 * g, cur = 2 * (g & 1), nxt = 2 - cur;
     load_scales(na, nx, ny, g + 1);
     bload(0, st + 2);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the MFMAs
-    stage(0, I0(), I0(), 4 * g + PF, true);
-    bstore(1, 1);
-    __syncthreads();
     bload(1, st + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    stage(1, J2(), I2(), 4 * g + 2 + PF, true);
-    bstore(0, 0);  // buffer 0 was last read before the barrier above
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the MFMAs
+    stage(cur, I0(), I0(), 4 * g + PF, true);
+    stage(cur + 1, J2(), I2(), 4 * g + 2 + PF, true);
+    bstore(0, nxt);
+    bstore(1, nxt + 1);
     __syncthreads();
     rotate_scales();
   }
-  if (NS & 1) stage(0, I0(), I0(), 0, false);  // last half group (K % 256 == 128)
+  if (NS & 1) stage(2 * (NG2 & 1), I0(), I0(), 0, false);  // last half group (K % 256 == 128)
 
   // ---- epilogue ------------------------------------------------------------
   if (!GATE_UP) {
@@ -392,7 +396,7 @@ hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc
   // (pair-row stages, row maps) share the 160 KB
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
-    const int cap = 160 * 1024 - 2 * B_STAGE - 2 * BM * 4 - 1024;
+    const int cap = 160 * 1024 - 4 * B_STAGE - 2 * BM * 4 - 1024;
     hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, cap);
     if (e == hipSuccess)
