@@ -171,7 +171,7 @@ int moe_route(const moe_config* cfg, const void* x, const float* router_w, const
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
   float* partial = at<float>(workspace, p.logits);
-  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, s));
+  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, 0, nullptr, nullptr, s));
   MOE_TRY(moe_k_topk_quant(cfg->x_dtype, partial, router_bias, x, cfg->T, cfg->H, cfg->E, cfg->top_k, 0, 0, topk_ids,
                            topk_w, nullptr, nullptr, s));
   return MOE_OK;
@@ -282,10 +282,15 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   if (!routed) {
     // route: partial logits, then top-k with the quantization of x
     MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
-    MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, s));
+    // small batches quantize x in the router's launch (off the top-k
+    // kernel's critical path), larger ones in the top-k kernel
+    const bool qr = moe_k_router_quantizes_x(T, H);
+    MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, mx, qr ? xq : nullptr,
+                                 qr ? (uint8_t*)xs : nullptr, s));
     MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
     MOE_TRY(mark(2 * MOE_STAGE_TOPK));
-    MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, 1, mx, ids, w, xq, (uint8_t*)xs, s));
+    MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, qr ? 0 : 1, mx, ids, w, xq,
+                             (uint8_t*)xs, s));
     MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
     MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
     MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));

@@ -15,8 +15,11 @@ hipError_t moe_k_unpack(int which, int E, int N, int K, const uint8_t* pcodes, c
 // route.hip
 int moe_k_router_slices(int T, int H);
 size_t moe_k_router_partial_bytes(int T, int H, int E);
+// With xq non-NULL (small batches only: moe_k_router_quantizes_x) the same
+// launch also quantizes x (int8 FP8-pair rows + scale, or MXFP4 if mx).
 hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
-                                hipStream_t st);
+                                int mx, uint8_t* xq, uint8_t* xs, hipStream_t st);
+int moe_k_router_quantizes_x(int T, int H);
 hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
                             int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
                             hipStream_t st);

@@ -55,6 +55,116 @@ __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return moe::bf16_bits_to_f32(*p); }
 
+// Quantize one row of x with one wave: int8 as FP8 (hi, lo) planes
+// [2][K] + fp32 scale, or MXFP4 codes [K/2] + E8M0 scales [K/32]
+// (K % 256 == 0). Compact loops: four four-element units per lane per batch.
+template <typename XT>
+__device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K, int mx, uint8_t* __restrict__ q,
+                                            uint8_t* __restrict__ qs) {
+  const int lane = threadIdx.x & 63;
+  if (!mx) {
+    const int nu = K >> 8;  // four-element units per lane
+    float amax = 0.f;
+#pragma unroll 1
+    for (int u0 = 0; u0 < nu; u0 += 4) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u0 + u, nu - 1) * 64 + lane) * 4, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+    }
+    amax = moe::wave_max(amax);
+    const float s = amax / 127.0f;
+    if (lane == 0) *reinterpret_cast<float*>(qs) = s;
+#pragma unroll 1
+    for (int u = 0; u < nu; ++u) {
+      float v[4];
+      const size_t i = ((size_t)u * 64 + lane) * 4;
+      load4<XT>(row + i, v);
+      uint32_t hw = 0, lw = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float qq = 0.f;
+        if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
+        int hi, lo;
+        moe::split_int8((int)qq, hi, lo);
+        hw |= moe::small_int_to_e4m3(hi) << (8 * m);
+        lw |= moe::small_int_to_e4m3(lo) << (8 * m);
+      }
+      *reinterpret_cast<uint32_t*>(q + i) = hw;
+      *reinterpret_cast<uint32_t*>(q + K + i) = lw;
+    }
+  } else {
+#pragma unroll 1
+    for (int b = lane; b < K / 32; b += 64) {
+      float v[32];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) load4<XT>(row + b * 32 + i, v + i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = amax > 0.f ? moe::mx_scale_exp(amax) : 0;
+      *reinterpret_cast<uint4*>(q + b * 16) = amax > 0.f ? moe::mx_pack32(v, e) : make_uint4(0, 0, 0, 0);
+      qs[b] = (uint8_t)e;
+    }
+  }
+}
+
+// Quantize one row of x with a whole 256-thread workgroup (the arithmetic of
+// wave_quant_row): int8 in two passes over the row (amax, then the FP8 pair
+// planes), float4 units with four loads in flight per thread; MXFP4 one
+// 32-block per thread. red: 4 floats of LDS.
+template <typename XT>
+__device__ __forceinline__ void block_quant_row(const XT* __restrict__ row, int K, int mx, uint8_t* __restrict__ q,
+                                                uint8_t* __restrict__ qs, float* red) {
+  const int tid = threadIdx.x;
+  if (mx) {
+    for (int b = tid; b < K / 32; b += 256) {
+      float v[32];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) load4<XT>(row + b * 32 + i, v + i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const int e = amax > 0.f ? moe::mx_scale_exp(amax) : 0;
+      *reinterpret_cast<uint4*>(q + b * 16) = amax > 0.f ? moe::mx_pack32(v, e) : make_uint4(0, 0, 0, 0);
+      qs[b] = (uint8_t)e;
+    }
+    return;
+  }
+  float amax = 0.f;
+#pragma unroll 4
+  for (int i = tid * 4; i < K; i += 1024) {
+    float v[4];
+    load4<XT>(row + i, v);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  amax = moe::wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  if (tid == 0) *reinterpret_cast<float*>(qs) = s;
+#pragma unroll 4
+  for (int i = tid * 4; i < K; i += 1024) {
+    float v[4];
+    load4<XT>(row + i, v);
+    uint32_t hw = 0, lw = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float qq = 0.f;
+      if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
+      int hi, lo;
+      moe::split_int8((int)qq, hi, lo);
+      hw |= moe::small_int_to_e4m3(hi) << (8 * m);
+      lw |= moe::small_int_to_e4m3(lo) << (8 * m);
+    }
+    *reinterpret_cast<uint32_t*>(q + i) = hw;
+    *reinterpret_cast<uint32_t*>(q + K + i) = lw;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Partial logits over one H slice. 256 threads = 16 x 16; tile (16 RA) tokens
 // x (16 RB) experts; KS k values per LDS stage; the next stage's global loads
@@ -64,7 +174,9 @@ __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return moe
 // ---------------------------------------------------------------------------
 template <typename XT, int RA, int RB, int KS, int CPS>
 __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
-                                                             float* __restrict__ partial, int T, int H, int E) {
+                                                             float* __restrict__ partial, int T, int H, int E,
+                                                             int mx, uint8_t* __restrict__ xq_out,
+                                                             uint8_t* __restrict__ xs_out) {
   static_assert(CPS == 1 || CPS == 8, "chunks per slice");
   constexpr int TT = 16 * RA, TE = 16 * RB;
   constexpr int NX = TT * KS / 4 / 256, NW = TE * KS / 4 / 256;  // float4 groups per thread
@@ -76,6 +188,18 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
   __shared__ __attribute__((aligned(16))) float ws[KS][TE + 4];
   const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, slice = blockIdx.z;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  if (CPS == 1 && slice >= 64) {
+    // the quantization of x, which the routing does not need, in workgroups
+    // of the same launch: one token row per workgroup
+    __shared__ float red[4];
+    const int t = (slice - 64) * gridDim.x + blockIdx.x;
+    if (t < T) {
+      const size_t qrow = mx ? (size_t)H / 2 : (size_t)2 * H;
+      const size_t srow = mx ? (size_t)H / 32 : 4;
+      block_quant_row<XT>(x + (size_t)t * H, H, mx, xq_out + t * qrow, xs_out + t * srow, red);
+    }
+    return;
+  }
   const int L = H >> 6;
   const int kbeg = slice * CPS * L, kend = kbeg + CPS * L;
 
@@ -243,62 +367,6 @@ __device__ __forceinline__ float finish_logit(const float* __restrict__ partial,
 #pragma unroll
     for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
   return bias ? v[0] + bias[e] : v[0];
-}
-
-// Quantize one row of x with one wave: int8 as FP8 (hi, lo) planes
-// [2][K] + fp32 scale, or MXFP4 codes [K/2] + E8M0 scales [K/32]
-// (K % 256 == 0). Compact loops: four four-element units per lane per batch.
-template <typename XT>
-__device__ __forceinline__ void wave_quant_row(const XT* __restrict__ row, int K, int mx, uint8_t* __restrict__ q,
-                                            uint8_t* __restrict__ qs) {
-  const int lane = threadIdx.x & 63;
-  if (!mx) {
-    const int nu = K >> 8;  // four-element units per lane
-    float amax = 0.f;
-#pragma unroll 1
-    for (int u0 = 0; u0 < nu; u0 += 4) {
-      float v[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u0 + u, nu - 1) * 64 + lane) * 4, v[u]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
-    }
-    amax = moe::wave_max(amax);
-    const float s = amax / 127.0f;
-    if (lane == 0) *reinterpret_cast<float*>(qs) = s;
-#pragma unroll 1
-    for (int u = 0; u < nu; ++u) {
-      float v[4];
-      const size_t i = ((size_t)u * 64 + lane) * 4;
-      load4<XT>(row + i, v);
-      uint32_t hw = 0, lw = 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float qq = 0.f;
-        if (amax != 0.f) qq = fminf(fmaxf(__builtin_rintf(v[m] / s), -127.f), 127.f);
-        int hi, lo;
-        moe::split_int8((int)qq, hi, lo);
-        hw |= moe::small_int_to_e4m3(hi) << (8 * m);
-        lw |= moe::small_int_to_e4m3(lo) << (8 * m);
-      }
-      *reinterpret_cast<uint32_t*>(q + i) = hw;
-      *reinterpret_cast<uint32_t*>(q + K + i) = lw;
-    }
-  } else {
-#pragma unroll 1
-    for (int b = lane; b < K / 32; b += 64) {
-      float v[32];
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) load4<XT>(row + b * 32 + i, v + i);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      const int e = amax > 0.f ? moe::mx_scale_exp(amax) : 0;
-      *reinterpret_cast<uint4*>(q + b * 16) = amax > 0.f ? moe::mx_pack32(v, e) : make_uint4(0, 0, 0, 0);
-      qs[b] = (uint8_t)e;
-    }
-  }
 }
 
 // Wave-wide max / min of a uint32 by DPP: row shifts build each 16-lane
@@ -495,23 +563,24 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
 }
 
 template <typename XT>
-hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, hipStream_t st) {
+hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, int mx, uint8_t* xq,
+                          uint8_t* xs, hipStream_t st) {
   const int L = H / 64;  // chunk length, a multiple of 4
   if (T <= 64 && L % 64 == 0 && L <= 256) {
-    // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range
-    if (T <= 16) {
-      dim3 grid((E + 15) / 16, 1, 64);
-      router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
-    } else if (T <= 32) {
-      dim3 grid((E + 15) / 16, 1, 64);
-      router_partial_kernel<XT, 2, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
-    } else {
-      dim3 grid((E + 15) / 16, 1, 64);
-      router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
-    }
+    // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range; with
+    // xq, slices 64.. quantize x (one token row per workgroup)
+    const int ex = (E + 15) / 16;
+    dim3 grid(ex, 1, 64 + (xq ? (T + ex - 1) / ex : 0));
+    if (T <= 16)
+      router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    else if (T <= 32)
+      router_partial_kernel<XT, 2, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    else
+      router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
   } else {
+    if (xq) return hipErrorInvalidValue;  // large batches quantize x in the top-k kernel
     dim3 grid((E + 63) / 64, (T + 63) / 64, 8);
-    router_partial_kernel<XT, 4, 4, 32, 8><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+    router_partial_kernel<XT, 4, 4, 32, 8><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, 0, nullptr, nullptr);
   }
   return hipGetLastError();
 }
@@ -526,11 +595,13 @@ int moe_k_router_slices(int T, int H) {
 size_t moe_k_router_partial_bytes(int T, int H, int E) { return (size_t)moe_k_router_slices(T, H) * T * E * 4; }
 
 hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
-                                hipStream_t st) {
+                                int mx, uint8_t* xq, uint8_t* xs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (x_dtype == 0) return launch_partial<float>((const float*)x, wr, partial, T, H, E, st);
-  return launch_partial<uint16_t>((const uint16_t*)x, wr, partial, T, H, E, st);
+  if (x_dtype == 0) return launch_partial<float>((const float*)x, wr, partial, T, H, E, mx, xq, xs, st);
+  return launch_partial<uint16_t>((const uint16_t*)x, wr, partial, T, H, E, mx, xq, xs, st);
 }
+
+int moe_k_router_quantizes_x(int T, int H) { return moe_k_router_slices(T, H) == 64; }
 
 hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
                             int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
