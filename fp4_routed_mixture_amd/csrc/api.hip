@@ -69,7 +69,7 @@ Plan make_plan(const moe_config* c) {
     off += up256(bytes);
     return o;
   };
-  p.logits = take(moe_k_router_partial_bytes(T, H, E));
+  p.logits = take(moe_k_router_partial_bytes(T, H, E, k));
   p.ids = take((size_t)p.P * 4);
   p.w = take((size_t)p.P * 4);
   p.xq = take(mx ? (size_t)T * H / 2 : (size_t)T * 2 * H);
@@ -167,11 +167,12 @@ int moe_route(const moe_config* cfg, const void* x, const float* router_w, const
   if (!x || !router_w || !topk_ids || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
   Plan p = make_plan(cfg);
-  if (workspace_bytes < p.logits + moe_k_router_partial_bytes(cfg->T, cfg->H, cfg->E))
+  if (workspace_bytes < p.logits + moe_k_router_partial_bytes(cfg->T, cfg->H, cfg->E, cfg->top_k))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
   float* partial = at<float>(workspace, p.logits);
-  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, 0, nullptr, nullptr, s));
+  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, cfg->top_k, 0, nullptr,
+                               nullptr, s));
   MOE_TRY(moe_k_topk_quant(cfg->x_dtype, partial, router_bias, x, cfg->T, cfg->H, cfg->E, cfg->top_k, 0, 0, topk_ids,
                            topk_w, nullptr, nullptr, s));
   return MOE_OK;
@@ -279,20 +280,27 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   auto mark = [&](int i) -> hipError_t { return ev && ev[i] ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
 
 
+  // small batches whose routing and sort fit one workgroup run them in one
+  // kernel (the top-k stage), and the sort stage is empty
+  const bool route_sorts = !routed && moe_k_route_sort_fits(T, H, E, k);
   if (!routed) {
     // route: partial logits, then top-k with the quantization of x
     MOE_TRY(mark(2 * MOE_STAGE_ROUTER));
     // small batches quantize x in the router's launch (off the top-k
     // kernel's critical path), larger ones in the top-k kernel
-    const bool qr = moe_k_router_quantizes_x(T, H);
-    MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, mx, qr ? xq : nullptr,
+    const bool qr = moe_k_router_quantizes_x(T, H, E, k);
+    MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, logits, T, H, E, k, mx, qr ? xq : nullptr,
                                  qr ? (uint8_t*)xs : nullptr, s));
     MOE_TRY(mark(2 * MOE_STAGE_ROUTER + 1));
     MOE_TRY(mark(2 * MOE_STAGE_TOPK));
-    MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, qr ? 0 : 1, mx, ids, w, xq,
-                             (uint8_t*)xs, s));
+    if (route_sorts)
+      MOE_TRY(moe_k_route_sort_small(logits, router_bias, T, E, k, p.block_m, ids, w, counts, offsets, sorted, pos,
+                                     tiles, ntiles, s));
+    else
+      MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, qr ? 0 : 1, mx, ids, w, xq,
+                               (uint8_t*)xs, s));
     MOE_TRY(mark(2 * MOE_STAGE_TOPK + 1));
-    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // fused into the top-k kernel
+    MOE_TRY(mark(2 * MOE_STAGE_QUANT_X));  // in the router launch or the top-k kernel
     MOE_TRY(mark(2 * MOE_STAGE_QUANT_X + 1));
   } else {
     // the caller's routing (ids clamped into [0, E) so that no id addresses
@@ -311,7 +319,8 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   }
   // sort
   MOE_TRY(mark(2 * MOE_STAGE_SORT));
-  MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
+  if (!route_sorts)
+    MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
   MOE_TRY(mark(2 * MOE_STAGE_SORT + 1));
   // expert GEMMs
   if (mx) {

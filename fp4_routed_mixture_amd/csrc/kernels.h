@@ -13,13 +13,19 @@ hipError_t moe_k_unpack(int which, int E, int N, int K, const uint8_t* pcodes, c
                         uint8_t* codes, uint8_t* scales, hipStream_t st);
 
 // route.hip
-int moe_k_router_slices(int T, int H);
-size_t moe_k_router_partial_bytes(int T, int H, int E);
+int moe_k_router_slices(int T, int H, int E, int K);
+size_t moe_k_router_partial_bytes(int T, int H, int E, int K);
 // With xq non-NULL (small batches only: moe_k_router_quantizes_x) the same
 // launch also quantizes x (int8 FP8-pair rows + scale, or MXFP4 if mx).
 hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
-                                int mx, uint8_t* xq, uint8_t* xs, hipStream_t st);
-int moe_k_router_quantizes_x(int T, int H);
+                                int K, int mx, uint8_t* xq, uint8_t* xs, hipStream_t st);
+int moe_k_router_quantizes_x(int T, int H, int E, int K);
+// Tiny batches (moe_k_router_slices == 16): routing and the expert sort (the
+// outputs of moe_k_sort) in one single-workgroup kernel.
+int moe_k_route_sort_fits(int T, int H, int E, int K);
+hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T, int E, int K, int block_m,
+                                  int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, hipStream_t st);
 hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
                             int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
                             hipStream_t st);

@@ -21,15 +21,23 @@
 // Small batches (T <= 64) keep all 64 chunk sums, partial[64][T][E] (one
 // chunk per workgroup, so each workgroup loads its operands once, and writes
 // 64-byte runs of adjacent experts), and finish the whole tree in
-// topk_quant_token, one workgroup per token, which also quantizes the token's
-// row of x. Larger batches keep 8 slice sums; topk_quant uses one wave per
-// token.
+// topk_quant_token, one workgroup per token; extra workgroups of the router's
+// launch quantize x. Tiny batches (T <= 16, T E <= 4096) use 16 slices of 4
+// chunks instead (a workgroup adds its 4 chunk sums as tree levels 1-2), and
+// route_sort_small finishes the top four levels, selects every token's
+// experts and sorts the pairs in one workgroup. Larger batches keep 8 slice
+// sums; topk_quant uses one wave per token.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
+#include "sort_dev.h"
 
 namespace {
 
-constexpr int NSLICE = 8;
+constexpr int NSLICE = 8;        // slices of large batches (8 chunks each)
+constexpr int NSLICE_SMALL = 64;  // slices of small batches (1 chunk each)
+constexpr int NSLICE_TINY = 16;   // slices of tiny batches (4 chunks each)
 constexpr int RKS = 32;  // k per LDS stage
 
 template <typename XT>
@@ -177,7 +185,8 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
                                                              float* __restrict__ partial, int T, int H, int E,
                                                              int mx, uint8_t* __restrict__ xq_out,
                                                              uint8_t* __restrict__ xs_out) {
-  static_assert(CPS == 1 || CPS == 8, "chunks per slice");
+  static_assert(CPS == 1 || CPS == 4 || CPS == 8, "chunks per slice");
+  constexpr int NSL = 64 / CPS;
   constexpr int TT = 16 * RA, TE = 16 * RB;
   constexpr int NX = TT * KS / 4 / 256, NW = TE * KS / 4 / 256;  // float4 groups per thread
   static_assert(NX >= 1 && NW >= 1, "tile too small for the stage");
@@ -188,11 +197,11 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
   __shared__ __attribute__((aligned(16))) float ws[KS][TE + 4];
   const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, slice = blockIdx.z;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  if (CPS == 1 && slice >= 64) {
+  if (CPS < 8 && slice >= NSL) {
     // the quantization of x, which the routing does not need, in workgroups
     // of the same launch: one token row per workgroup
     __shared__ float red[4];
-    const int t = (slice - 64) * gridDim.x + blockIdx.x;
+    const int t = (slice - NSL) * gridDim.x + blockIdx.x;
     if (t < T) {
       const size_t qrow = mx ? (size_t)H / 2 : (size_t)2 * H;
       const size_t srow = mx ? (size_t)H / 32 : 4;
@@ -249,11 +258,11 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
     if (k0 + KS < kend) fetch(k0 + KS);
     // Four k per group (L % 4 == 0, so a chunk never ends inside a group):
     // the group's LDS reads are issued together, then its fmas run in
-    // ascending k per output. With one chunk per slice (small batches: L is a
-    // multiple of KS) a chunk can only end with a stage, so the stage runs
-    // branch-free and fully unrolled; otherwise the chunk end is checked after
-    // every group (unrolling the 8-chunk slices measured slower: the hoisted
-    // reads halve the occupancy).
+    // ascending k per output. In the small-batch slices L is a multiple of KS,
+    // so a chunk can only end with a stage and the stage runs branch-free and
+    // fully unrolled; otherwise the chunk end is checked after every group
+    // (unrolling the large-batch tiles measured slower: the hoisted reads
+    // halve the occupancy).
     auto group = [&](int kk) {
       float xa[4][RA], wb[4][RB];
 #pragma unroll
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
           for (int b = 0; b < RB; ++b) acc[a][b] = __builtin_fmaf(xa[u][a], wb[u][b], acc[a][b]);
     };
     auto push = [&]() {
-      // push the chunk sums: chunk index within the slice = 3-bit counter
+      // push the chunk sums: chunk index within the slice = 2- or 3-bit counter
       const bool b0 = chunk & 1, b1 = chunk & 2, b2 = chunk & 4;
 #pragma unroll
       for (int a = 0; a < RA; ++a)
@@ -311,14 +320,14 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
               st1[a][b] = v;
             } else {
               v = st1[a][b] + v;
-              if (!b2) st2[a][b] = v;
-              else st2[a][b] = st2[a][b] + v;  // chunk 7: the slice total
+              if (CPS == 4 || !b2) st2[a][b] = v;  // CPS 4: chunk 3, the slice total
+              else st2[a][b] = st2[a][b] + v;      // CPS 8: chunk 7, the slice total
             }
           }
         }
       ++chunk;
     };
-    if (CPS == 1 && L % KS == 0) {
+    if (CPS < 8 && L % KS == 0) {
 #pragma unroll
       for (int kk = 0; kk < KS; kk += 4) group(kk);
       in_chunk += KS;
@@ -353,8 +362,17 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
 }
 
 // Logit of (t, e) from the NS slice sums of the slice-major layout
-// [NS][T][E] (NS = 8 or 64): the tree's remaining levels over the slices,
+// [NS][T][E] (NS = 8, 16 or 64): the tree's remaining levels over the slices,
 // then the bias. A wave's load of one slice reads adjacent experts.
+template <int NS>
+__device__ __forceinline__ float tree_sum(float* v) {
+#pragma unroll
+  for (int w = NS; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
+}
+
 template <int NS>
 __device__ __forceinline__ float finish_logit(const float* __restrict__ partial, const float* __restrict__ bias, int T,
                                               int E, int t, int e) {
@@ -362,11 +380,8 @@ __device__ __forceinline__ float finish_logit(const float* __restrict__ partial,
   const size_t st = (size_t)T * E, o = (size_t)t * E + e;
 #pragma unroll
   for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
-#pragma unroll
-  for (int w = NS; w > 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
-  return bias ? v[0] + bias[e] : v[0];
+  const float l = tree_sum<NS>(v);
+  return bias ? l + bias[e] : l;
 }
 
 // Wave-wide max / min of a uint32 by DPP: row shifts build each 16-lane
@@ -450,11 +465,11 @@ __device__ __forceinline__ float renorm_weight(const float* sel_s, int K, int j)
 
 // ---------------------------------------------------------------------------
 // Small batches: one 256-thread workgroup per token. Threads finish the
-// logits of the token's experts from the 64 chunk sums (the whole pairwise
-// tree), the sigmoid scores go to LDS, wave 0 selects the top k, and all
+// logits of the token's experts from the NS slice sums (the tree's top
+// levels), the sigmoid scores go to LDS, wave 0 selects the top k, and all
 // four waves quantize the token's row of x (int8 rows only).
 // ---------------------------------------------------------------------------
-template <typename XT>
+template <typename XT, int NS>
 __global__ __launch_bounds__(256) void topk_quant_token_kernel(const float* __restrict__ partial,
                                                                const float* __restrict__ bias, const XT* __restrict__ x,
                                                                int T, int H, int E, int K, int quant, int mx,
@@ -477,7 +492,7 @@ __global__ __launch_bounds__(256) void topk_quant_token_kernel(const float* __re
     for (int u = 0; u < 4; ++u) load4<XT>(row + ((size_t)min(u, nu - 1) * 256 + tid) * 4, v[u]);
   }
 #pragma unroll 1
-  for (int e = tid; e < E; e += 256) sc[e] = moe::sigmoid_fixed(finish_logit<64>(partial, bias, T, E, t, e));
+  for (int e = tid; e < E; e += 256) sc[e] = moe::sigmoid_fixed(finish_logit<NS>(partial, bias, T, E, t, e));
   float amax = 0.f;
   if (regs) {
 #pragma unroll
@@ -562,15 +577,102 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches, routing and sort in one 1024-thread workgroup (no hand-over
+// between workgroups): the logits of all T x E (token, expert) items from the
+// 16 four-chunk slice sums, their sigmoid scores in LDS, the top k of token t by wave
+// t % 16, then the stable expert sort of the P = T k pairs with the
+// arithmetic of the one-workgroup sort kernel. Dynamic LDS: max(T E scores,
+// the sort's E ceil(P / 32) mask words), then tot[E], offs[E + 1], tmp[1024].
+// ---------------------------------------------------------------------------
+constexpr int RS_ITEMS = 4;        // logits per thread per batch of loads
+constexpr int RS_MAX_TE = 4096;    // scores of a tiny batch
+
+__global__ __launch_bounds__(1024) void route_sort_small_kernel(
+    const float* __restrict__ partial, const float* __restrict__ bias, int T, int E, int K, int block_m,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ n_tiles) {
+  extern __shared__ int smem[];
+  __shared__ int ids_lds[moe::SB];
+  __shared__ int sel_id[16][16];
+  __shared__ float sel_s[16][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int TE = T * E, P = T * K, W = (P + 31) >> 5;
+  float* sc = reinterpret_cast<float*>(smem);
+  int* tot = smem + max(TE, E * W);
+  int* offs = tot + E;
+  int* tmp = offs + E + 1;
+
+  // scores: each thread's RS_ITEMS items of a batch have all their slice
+  // loads in flight together (indices clamped, so no load is conditional)
+  for (int i0 = 0; i0 < TE; i0 += 1024 * RS_ITEMS) {
+    float v[RS_ITEMS][NSLICE_TINY];
+#pragma unroll
+    for (int u = 0; u < RS_ITEMS; ++u) {
+      const int ic = min(i0 + u * 1024 + tid, TE - 1);
+#pragma unroll
+      for (int sl = 0; sl < NSLICE_TINY; ++sl) v[u][sl] = partial[(size_t)sl * TE + ic];
+    }
+#pragma unroll
+    for (int u = 0; u < RS_ITEMS; ++u) {
+      const int i = i0 + u * 1024 + tid;
+      if (i < TE) {
+        const float l = tree_sum<NSLICE_TINY>(v[u]);
+        sc[i] = moe::sigmoid_fixed(bias ? l + bias[i % E] : l);
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int t = wave; t < T; t += 16) {
+    wave_topk(sc + (size_t)t * E, E, K, sel_id[wave], sel_s[wave]);
+    // lane 0 wrote the wave's own LDS rows: wave-level ordering suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < K) {
+      const int id = sel_id[wave][lane];
+      ids_out[(size_t)t * K + lane] = id;
+      w_out[(size_t)t * K + lane] = renorm_weight(sel_s[wave], K, lane);
+      ids_lds[t * K + lane] = id;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();
+
+  // the sort (the score region is reused for the expert bitmasks)
+  const bool valid = tid < P;
+  const int id = valid ? ids_lds[tid] : 0;
+  int rank;
+  moe::block_rank(id, valid, P, E, reinterpret_cast<uint32_t*>(smem), tot, rank);
+  moe::scan_offsets(tot, E, block_m, offs, tmp);
+  if (valid) {
+    const int p = offs[id] + rank;
+    sorted[p] = tid;
+    pos[tid] = p;
+  }
+  for (int e = tid; e < E; e += blockDim.x) counts[e] = tot[e];
+  for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
+  moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+}
+
 template <typename XT>
-hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, int mx, uint8_t* xq,
-                          uint8_t* xs, hipStream_t st) {
-  const int L = H / 64;  // chunk length, a multiple of 4
-  if (T <= 64 && L % 64 == 0 && L <= 256) {
+hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, int ns, int mx,
+                          uint8_t* xq, uint8_t* xs, hipStream_t st) {
+  if (ns == NSLICE_TINY) {
+    // four chunks per workgroup (T <= 16 here), one LDS stage (64 k) per
+    // chunk sub-range; with xq, slices 16.. quantize x (a token row each)
+    const int ex = (E + 15) / 16;
+    dim3 grid(ex, 1, NSLICE_TINY + (xq ? (T + ex - 1) / ex : 0));
+    router_partial_kernel<XT, 1, 1, 64, 4><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+  } else if (ns == NSLICE_SMALL) {
     // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range; with
     // xq, slices 64.. quantize x (one token row per workgroup)
     const int ex = (E + 15) / 16;
-    dim3 grid(ex, 1, 64 + (xq ? (T + ex - 1) / ex : 0));
+    dim3 grid(ex, 1, NSLICE_SMALL + (xq ? (T + ex - 1) / ex : 0));
     if (T <= 16)
       router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
     else if (T <= 32)
@@ -587,34 +689,48 @@ hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, i
 
 }  // namespace
 
-int moe_k_router_slices(int T, int H) {
+int moe_k_router_slices(int T, int H, int E, int K) {
   const int L = H / 64;
-  return (T <= 64 && L % 64 == 0 && L <= 256) ? 64 : 8;
+  if (!(T <= 64 && L % 64 == 0 && L <= 256)) return NSLICE;
+  return (T <= 16 && T * E <= RS_MAX_TE && K <= 16 && E <= 1024) ? NSLICE_TINY : NSLICE_SMALL;
 }
 
-size_t moe_k_router_partial_bytes(int T, int H, int E) { return (size_t)moe_k_router_slices(T, H) * T * E * 4; }
+size_t moe_k_router_partial_bytes(int T, int H, int E, int K) {
+  return (size_t)moe_k_router_slices(T, H, E, K) * T * E * 4;
+}
 
 hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
-                                int mx, uint8_t* xq, uint8_t* xs, hipStream_t st) {
+                                int K, int mx, uint8_t* xq, uint8_t* xs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (x_dtype == 0) return launch_partial<float>((const float*)x, wr, partial, T, H, E, mx, xq, xs, st);
-  return launch_partial<uint16_t>((const uint16_t*)x, wr, partial, T, H, E, mx, xq, xs, st);
+  const int ns = moe_k_router_slices(T, H, E, K);
+  if (x_dtype == 0) return launch_partial<float>((const float*)x, wr, partial, T, H, E, ns, mx, xq, xs, st);
+  return launch_partial<uint16_t>((const uint16_t*)x, wr, partial, T, H, E, ns, mx, xq, xs, st);
 }
 
-int moe_k_router_quantizes_x(int T, int H) { return moe_k_router_slices(T, H) == 64; }
+int moe_k_router_quantizes_x(int T, int H, int E, int K) { return moe_k_router_slices(T, H, E, K) != NSLICE; }
 
 hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
                             int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
                             hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (moe_k_router_slices(T, H) == 64) {
+  const int ns = moe_k_router_slices(T, H, E, K);
+  if (ns != NSLICE) {
     // per-token workgroups
-    if (x_dtype == 0)
-      topk_quant_token_kernel<float><<<T, 256, 0, st>>>(partial, bias, (const float*)x, T, H, E, K, quant, mx, ids, w,
-                                                        xq, xs);
-    else
-      topk_quant_token_kernel<uint16_t><<<T, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H, E, K, quant, mx,
-                                                           ids, w, xq, xs);
+    if (x_dtype == 0) {
+      if (ns == NSLICE_TINY)
+        topk_quant_token_kernel<float, NSLICE_TINY><<<T, 256, 0, st>>>(partial, bias, (const float*)x, T, H, E, K,
+                                                                       quant, mx, ids, w, xq, xs);
+      else
+        topk_quant_token_kernel<float, NSLICE_SMALL><<<T, 256, 0, st>>>(partial, bias, (const float*)x, T, H, E, K,
+                                                                        quant, mx, ids, w, xq, xs);
+    } else {
+      if (ns == NSLICE_TINY)
+        topk_quant_token_kernel<uint16_t, NSLICE_TINY><<<T, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H, E,
+                                                                          K, quant, mx, ids, w, xq, xs);
+      else
+        topk_quant_token_kernel<uint16_t, NSLICE_SMALL><<<T, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H,
+                                                                           E, K, quant, mx, ids, w, xq, xs);
+    }
     return hipGetLastError();
   }
   const int blocks = (T + 3) / 4;
@@ -624,5 +740,27 @@ hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias
   else
     topk_quant_kernel<uint16_t><<<blocks, 256, 0, st>>>(partial, bias, (const uint16_t*)x, T, H, E, K, quant, mx, ids,
                                                         w, xq, xs);
+  return hipGetLastError();
+}
+
+int moe_k_route_sort_fits(int T, int H, int E, int K) { return moe_k_router_slices(T, H, E, K) == NSLICE_TINY; }
+
+hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T, int E, int K, int block_m,
+                                  int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (T * K > moe::SB || K > 16 || E > 1024 || T * E > RS_MAX_TE) return hipErrorInvalidValue;
+  // above 64 KB of LDS a kernel must opt in (gfx950: 160 KB per workgroup)
+  static bool lds_opt_in = false;
+  if (!lds_opt_in) {
+    hipError_t e = hipFuncSetAttribute((const void*)route_sort_small_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+    if (e != hipSuccess) return e;
+    lds_opt_in = true;
+  }
+  const int P = T * K, W = (P + 31) / 32;
+  const size_t lds = (size_t)(std::max(T * E, E * W) + E + E + 1 + 1024) * 4;
+  route_sort_small_kernel<<<1, 1024, lds, st>>>(partial, bias, T, E, K, block_m, ids, w, counts, offsets, sorted, pos,
+                                                tile_expert, n_tiles);
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@ import oracle
 from fp4_routed_mixture_amd import binding as B
 from fp4_routed_mixture_amd import synth as S
 from fp4_routed_mixture_amd import synth_device as SD
-from gpu_util import require_gpu, sha
+from gpu_util import require_gpu, run_forward, sha
 
 pytestmark = pytest.mark.gpu
 
@@ -148,6 +148,39 @@ def test_sort_bitexact(P, E, block_m, dist):
     assert np.array_equal(g["pos"], o["pos"])
     assert g["n_tiles"] == o["n_tiles"]
     assert np.array_equal(g["tiles"][: o["n_tiles"]], o["tile_expert"])
+
+
+# Tiny batches (T <= 16, T * E <= 4096) route and sort in one workgroup from
+# 16 four-chunk slice sums; other small batches use 64 one-chunk slices and
+# the separate top-k and sort kernels. The cases span that switch.
+ROUTE_SORT_CASES = [
+    ("rs_t1", 1, 4096, 256, 256, 6, S.ACT_INT8, False),
+    ("rs_t4", 4, 4096, 256, 256, 6, S.ACT_INT8, False),
+    ("rs_t16_zipf", 16, 4096, 256, 256, 6, S.ACT_INT8, True),
+    ("rs_t4_e1024", 4, 4096, 256, 1024, 8, S.ACT_INT8, False),
+    ("rs_t8_e512_k16_mx", 8, 8192, 256, 512, 16, S.ACT_MXFP4, True),
+    ("rs_t16_e512", 16, 4096, 256, 512, 6, S.ACT_INT8, False),
+    ("rs_t17", 17, 4096, 256, 64, 4, S.ACT_INT8, False),
+    ("rs_t32_zipf", 32, 4096, 256, 256, 6, S.ACT_INT8, True),
+    ("rs_t64_zipf", 64, 4096, 256, 256, 6, S.ACT_INT8, True),
+]
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k,act,zipf", ROUTE_SORT_CASES)
+def test_forward_routing_and_sort_bitexact(name, T, H, I, E, k, act, zipf):
+    """The routing and the sort arrays a whole-layer call produces (its taps)
+    equal the oracle's route and sort bit for bit."""
+    w = S.Workload(name, T, H, I, E, k, S.X_BF16, act, zipf, 41)
+    print(f"[route+sort] {S.describe(w)}", flush=True)
+    g = run_forward(w, SD.load_layer(w), SD.activations(w), taps=True)
+    ids_o, w_o = oracle.route(S.activations(w), S.router_weights(w), S.router_bias(w), k)
+    assert np.array_equal(g["ids"], ids_o)
+    assert np.array_equal(g["w"].view(np.uint32), w_o.view(np.uint32))
+    o = oracle.sort(ids_o, E, g["block_m"])
+    assert np.array_equal(g["counts"], o["counts"])
+    assert np.array_equal(g["offsets"], o["offsets"])
+    assert np.array_equal(g["sorted_pairs"][: o["total"]], o["sorted"])
+    assert np.array_equal(g["pair_pos"][: T * k], o["pos"])
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_t4", "prefill_t4604_zipf"])
