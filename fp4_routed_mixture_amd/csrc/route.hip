@@ -258,11 +258,11 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
     if (k0 + KS < kend) fetch(k0 + KS);
     // Four k per group (L % 4 == 0, so a chunk never ends inside a group):
     // the group's LDS reads are issued together, then its fmas run in
-    // ascending k per output. In the small-batch slices L is a multiple of KS,
-    // so a chunk can only end with a stage and the stage runs branch-free and
-    // fully unrolled; otherwise the chunk end is checked after every group
-    // (unrolling the large-batch tiles measured slower: the hoisted reads
-    // halve the occupancy).
+    // ascending k per output. Where L is a multiple of KS (the one-chunk
+    // small-batch slices) a chunk can only end with a stage, so the stage
+    // runs branch-free and fully unrolled; otherwise the chunk end is checked
+    // after every group (unrolling the large-batch tiles measured slower: the
+    // hoisted reads halve the occupancy).
     auto group = [&](int kk) {
       float xa[4][RA], wb[4][RB];
 #pragma unroll
@@ -585,8 +585,30 @@ __global__ __launch_bounds__(256) void topk_quant_kernel(const float* __restrict
 // arithmetic of the one-workgroup sort kernel. Dynamic LDS: max(T E scores,
 // the sort's E ceil(P / 32) mask words), then tot[E], offs[E + 1], tmp[1024].
 // ---------------------------------------------------------------------------
-constexpr int RS_ITEMS = 4;        // logits per thread per batch of loads
-constexpr int RS_MAX_TE = 4096;    // scores of a tiny batch
+constexpr int RS_MAX_TE = 4096;  // scores of a tiny batch (4 per thread)
+
+// Sigmoid scores of items tid, tid + 1024, ... (NI of them, NI * 1024 >= TE)
+// into sc[TE].
+template <int NI>
+__device__ __forceinline__ void score_items(const float* __restrict__ partial, const float* __restrict__ bias, int TE,
+                                            int E, float* sc) {
+  const int tid = threadIdx.x;
+  float v[NI][NSLICE_TINY];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int ic = min(u * 1024 + tid, TE - 1);
+#pragma unroll
+    for (int sl = 0; sl < NSLICE_TINY; ++sl) v[u][sl] = partial[(size_t)sl * TE + ic];
+  }
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = u * 1024 + tid;
+    if (i < TE) {
+      const float l = tree_sum<NSLICE_TINY>(v[u]);
+      sc[i] = moe::sigmoid_fixed(bias ? l + bias[i % E] : l);
+    }
+  }
+}
 
 __global__ __launch_bounds__(1024) void route_sort_small_kernel(
     const float* __restrict__ partial, const float* __restrict__ bias, int T, int E, int K, int block_m,
@@ -604,25 +626,11 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
   int* offs = tot + E;
   int* tmp = offs + E + 1;
 
-  // scores: each thread's RS_ITEMS items of a batch have all their slice
-  // loads in flight together (indices clamped, so no load is conditional)
-  for (int i0 = 0; i0 < TE; i0 += 1024 * RS_ITEMS) {
-    float v[RS_ITEMS][NSLICE_TINY];
-#pragma unroll
-    for (int u = 0; u < RS_ITEMS; ++u) {
-      const int ic = min(i0 + u * 1024 + tid, TE - 1);
-#pragma unroll
-      for (int sl = 0; sl < NSLICE_TINY; ++sl) v[u][sl] = partial[(size_t)sl * TE + ic];
-    }
-#pragma unroll
-    for (int u = 0; u < RS_ITEMS; ++u) {
-      const int i = i0 + u * 1024 + tid;
-      if (i < TE) {
-        const float l = tree_sum<NSLICE_TINY>(v[u]);
-        sc[i] = moe::sigmoid_fixed(bias ? l + bias[i % E] : l);
-      }
-    }
-  }
+  // scores: the items of a thread have all their slice loads in flight
+  // together (indices clamped, so no load is conditional)
+  if (TE > 2048) score_items<4>(partial, bias, TE, E, sc);
+  else if (TE > 1024) score_items<2>(partial, bias, TE, E, sc);
+  else score_items<1>(partial, bias, TE, E, sc);
   __syncthreads();
 
   for (int t = wave; t < T; t += 16) {
@@ -663,11 +671,12 @@ template <typename XT>
 hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, int ns, int mx,
                           uint8_t* xq, uint8_t* xs, hipStream_t st) {
   if (ns == NSLICE_TINY) {
-    // four chunks per workgroup (T <= 16 here), one LDS stage (64 k) per
-    // chunk sub-range; with xq, slices 16.. quantize x (a token row each)
+    // four chunks per workgroup (T <= 16 here) in LDS stages of 256 k, so
+    // that a slice's loads are in flight together; with xq, slices 16..
+    // quantize x (a token row each)
     const int ex = (E + 15) / 16;
     dim3 grid(ex, 1, NSLICE_TINY + (xq ? (T + ex - 1) / ex : 0));
-    router_partial_kernel<XT, 1, 1, 64, 4><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    router_partial_kernel<XT, 1, 1, 256, 4><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
   } else if (ns == NSLICE_SMALL) {
     // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range; with
     // xq, slices 64.. quantize x (one token row per workgroup)
