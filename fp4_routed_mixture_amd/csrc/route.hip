@@ -671,12 +671,13 @@ template <typename XT>
 hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, int H, int E, int ns, int mx,
                           uint8_t* xq, uint8_t* xs, hipStream_t st) {
   if (ns == NSLICE_TINY) {
-    // four chunks per workgroup (T <= 16 here) in LDS stages of 256 k, so
-    // that a slice's loads are in flight together; with xq, slices 16..
-    // quantize x (a token row each)
+    // four chunks per workgroup (T <= 16 here), one LDS stage (64 k) per
+    // chunk sub-range, so that each stage runs branch-free (stages of 256 k
+    // took the per-group chunk-end checks and measured slower); with xq,
+    // slices 16.. quantize x (a token row each)
     const int ex = (E + 15) / 16;
     dim3 grid(ex, 1, NSLICE_TINY + (xq ? (T + ex - 1) / ex : 0));
-    router_partial_kernel<XT, 1, 1, 256, 4><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    router_partial_kernel<XT, 1, 1, 64, 4><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
   } else if (ns == NSLICE_SMALL) {
     // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range; with
     // xq, slices 64.. quantize x (one token row per workgroup)
