@@ -11,7 +11,7 @@ import oracle
 from fp4_routed_mixture_amd import binding as B
 from fp4_routed_mixture_amd import synth as S
 from fp4_routed_mixture_amd import synth_device as SD
-from gpu_util import require_gpu, run_forward, sha
+from gpu_util import assert_close_rms, oracle_layer, require_gpu, run_forward, sha
 
 pytestmark = pytest.mark.gpu
 
@@ -154,23 +154,26 @@ def test_sort_bitexact(P, E, block_m, dist):
 # 16 four-chunk slice sums; other small batches use 64 one-chunk slices and
 # the separate top-k and sort kernels. The cases span that switch.
 ROUTE_SORT_CASES = [
-    ("rs_t1", 1, 4096, 256, 256, 6, S.ACT_INT8, False),
-    ("rs_t4", 4, 4096, 256, 256, 6, S.ACT_INT8, False),
-    ("rs_t16_zipf", 16, 4096, 256, 256, 6, S.ACT_INT8, True),
-    ("rs_t4_e1024", 4, 4096, 256, 1024, 8, S.ACT_INT8, False),
-    ("rs_t8_e512_k16_mx", 8, 8192, 256, 512, 16, S.ACT_MXFP4, True),
-    ("rs_t16_e512", 16, 4096, 256, 512, 6, S.ACT_INT8, False),
-    ("rs_t17", 17, 4096, 256, 64, 4, S.ACT_INT8, False),
-    ("rs_t32_zipf", 32, 4096, 256, 256, 6, S.ACT_INT8, True),
-    ("rs_t64_zipf", 64, 4096, 256, 256, 6, S.ACT_INT8, True),
+    ("rs_t1", 1, 4096, 256, 256, 6, S.X_BF16, S.ACT_INT8, False),
+    ("rs_t4", 4, 4096, 256, 256, 6, S.X_BF16, S.ACT_INT8, False),
+    ("rs_t4_f32", 4, 4096, 256, 256, 6, S.X_F32, S.ACT_INT8, False),
+    ("rs_t16_zipf", 16, 4096, 256, 256, 6, S.X_BF16, S.ACT_INT8, True),
+    ("rs_t4_e1024", 4, 4096, 256, 1024, 8, S.X_BF16, S.ACT_INT8, False),
+    ("rs_t8_e512_k16_mx", 8, 8192, 256, 512, 16, S.X_BF16, S.ACT_MXFP4, True),
+    ("rs_t3_f32_mx", 3, 4096, 256, 64, 4, S.X_F32, S.ACT_MXFP4, False),
+    ("rs_t16_e512", 16, 4096, 256, 512, 6, S.X_BF16, S.ACT_INT8, False),
+    ("rs_t17", 17, 4096, 256, 64, 4, S.X_BF16, S.ACT_INT8, False),
+    ("rs_t32_zipf", 32, 4096, 256, 256, 6, S.X_BF16, S.ACT_INT8, True),
+    ("rs_t64_zipf", 64, 4096, 256, 256, 6, S.X_BF16, S.ACT_INT8, True),
 ]
 
 
-@pytest.mark.parametrize("name,T,H,I,E,k,act,zipf", ROUTE_SORT_CASES)
-def test_forward_routing_and_sort_bitexact(name, T, H, I, E, k, act, zipf):
+@pytest.mark.parametrize("name,T,H,I,E,k,xd,act,zipf", ROUTE_SORT_CASES)
+def test_forward_routing_and_sort_bitexact(name, T, H, I, E, k, xd, act, zipf):
     """The routing and the sort arrays a whole-layer call produces (its taps)
-    equal the oracle's route and sort bit for bit."""
-    w = S.Workload(name, T, H, I, E, k, S.X_BF16, act, zipf, 41)
+    equal the oracle's route and sort bit for bit, and so does the output in
+    int8 mode (MXFP4: within the tolerance)."""
+    w = S.Workload(name, T, H, I, E, k, xd, act, zipf, 41)
     print(f"[route+sort] {S.describe(w)}", flush=True)
     g = run_forward(w, SD.load_layer(w), SD.activations(w), taps=True)
     ids_o, w_o = oracle.route(S.activations(w), S.router_weights(w), S.router_bias(w), k)
@@ -181,6 +184,11 @@ def test_forward_routing_and_sort_bitexact(name, T, H, I, E, k, act, zipf):
     assert np.array_equal(g["offsets"], o["offsets"])
     assert np.array_equal(g["sorted_pairs"][: o["total"]], o["sorted"])
     assert np.array_equal(g["pair_pos"][: T * k], o["pos"])
+    ref = oracle_layer(w, S.activations(w))
+    if act == S.ACT_INT8:
+        assert np.array_equal(g["out"], ref["out"])
+    else:
+        assert_close_rms(g["out"], ref["out"])
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode_t4", "prefill_t4604_zipf"])
