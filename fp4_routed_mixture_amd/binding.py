@@ -24,7 +24,8 @@ STAGES = ["router", "topk", "quant_x", "sort", "gate_up", "requant", "down", "co
 
 # every function that include/fp4moe.h declares
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_workspace_size",
-           "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_sort", "moe_quantize",
+           "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_router_logits", "moe_sort",
+           "moe_quantize",
            "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
            "moe_stack_workspace_size", "moe_forward_stack"]
 
@@ -74,6 +75,7 @@ def lib():
             "moe_prepack": (C.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "moe_unpack": (C.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
             "moe_route": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_router_logits": (C.c_int, [cfgp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_sort": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_quantize": (C.c_int, [cfgp, i32, i32, i32, vp, vp, vp, vp]),
             "moe_forward": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -160,6 +162,13 @@ def moe_route(cfg, x, router_w, router_bias, topk_ids, topk_w, workspace, stream
     _check(lib().moe_route(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(topk_ids), _p(topk_w),
                            _p(workspace), workspace.numel() if workspace is not None else 0, _s(stream)),
            "moe_route")
+
+
+def moe_router_logits(cfg, x, router_w, router_bias, logits, workspace, stream=None):
+    """Router logits fp32 [T][E] (before the sigmoid) into the device tensor logits."""
+    _check(lib().moe_router_logits(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(logits), _p(workspace),
+                                   workspace.numel() if workspace is not None else 0, _s(stream)),
+           "moe_router_logits")
 
 
 def moe_sort(cfg, block_m, topk_ids, counts, offsets, sorted_pairs, pair_pos, tile_expert, n_tiles,

@@ -178,6 +178,25 @@ int moe_route(const moe_config* cfg, const void* x, const float* router_w, const
   return MOE_OK;
 }
 
+int moe_router_logits(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                      float* logits, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !router_w || !logits || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  Plan p = make_plan(cfg);
+  const size_t need = p.logits + moe_k_router_partial_bytes(cfg->T, cfg->H, cfg->E, cfg->top_k);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlaps(workspace, need, logits, (size_t)cfg->T * cfg->E * 4)) return MOE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  float* partial = at<float>(workspace, p.logits);
+  MOE_TRY(moe_k_router_partial(cfg->x_dtype, x, router_w, partial, cfg->T, cfg->H, cfg->E, cfg->top_k, 0, nullptr,
+                               nullptr, s));
+  MOE_TRY(moe_k_finish_logits(partial, router_bias, cfg->T, cfg->H, cfg->E, cfg->top_k, logits, s));
+  return MOE_OK;
+}
+
 int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
              int32_t* sorted_pairs, int32_t* pair_pos, int32_t* tile_expert, int32_t* n_tiles, void* workspace,
              size_t workspace_bytes, void* stream) {

@@ -20,6 +20,9 @@ size_t moe_k_router_partial_bytes(int T, int H, int E, int K);
 hipError_t moe_k_router_partial(int x_dtype, const void* x, const float* wr, float* partial, int T, int H, int E,
                                 int K, int mx, uint8_t* xq, uint8_t* xs, hipStream_t st);
 int moe_k_router_quantizes_x(int T, int H, int E, int K);
+// logits[T][E] from the partial sums (the tree's remaining levels + bias).
+hipError_t moe_k_finish_logits(const float* partial, const float* bias, int T, int H, int E, int K, float* logits,
+                               hipStream_t st);
 // Tiny batches (moe_k_router_slices == 16): routing and the expert sort (the
 // outputs of moe_k_sort) in one single-workgroup kernel.
 int moe_k_route_sort_fits(int T, int H, int E, int K);

@@ -197,6 +197,16 @@ int moe_unpack(int32_t which, int32_t E, int32_t N, int32_t K,
 int moe_route(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
               int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The router logits alone, as moe_route computes them before the sigmoid:
+ * logits fp32 [T][E] (device, caller-owned, overwritten),
+ * l[t][e] = pdot(x[t], router_w[e]) + router_bias[e], where pdot splits H
+ * into 64 contiguous chunks, sums each chunk as a chain of fused
+ * multiply-adds in ascending k and adds the 64 chunk sums as a perfect
+ * pairwise tree in index order. Same shapes, workspace and errors as
+ * moe_route (logits must not overlap the workspace: MOE_ERR_ALIAS). */
+int moe_router_logits(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                      float* logits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ sort --
  * Expert sort (the gfx90a paper retunes it for prefill, abstract): group the P pairs
  * (p = t * top_k + j) by expert, keeping ascending p within an expert, each

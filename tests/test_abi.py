@@ -130,6 +130,9 @@ def test_other_entry_point_errors(L):
     assert L.moe_quantize(C.byref(c), 4, 128, 0, FAKE + 4, FAKE, FAKE, None) == 3
     assert L.moe_route(C.byref(c), None, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert L.moe_route(C.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, None) == 5
+    assert L.moe_router_logits(C.byref(c), None, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.moe_router_logits(C.byref(c), FAKE, FAKE, None, FAKE, FAKE, 10, None) == 5
+    assert L.moe_router_logits(C.byref(c), FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 4  # logits in workspace
     assert L.moe_prepack(0, 8, 256, 256, FAKE, FAKE, None, FAKE, FAKE + (1 << 20), None) == 4  # codes overlap
     assert L.moe_rmsnorm(2, 100, FAKE, FAKE + (1 << 20), None) == 2
     assert L.moe_rmsnorm(2, 128, FAKE, FAKE + 4, None) == 4

@@ -105,6 +105,44 @@ def test_router_kernels_agree(T):
     assert np.array_equal(wts.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
 
 
+# (T, H, E, x dtype): tiny batches (16 four-chunk slices), small batches (64
+# one-chunk slices), large batches on the matrix cores (H % 2048 == 0) and on
+# the VALU (other H); E not a multiple of a tile included.
+LOGIT_CASES = [(4, 4096, 256, S.X_BF16), (16, 4096, 256, S.X_F32), (17, 4096, 256, S.X_BF16),
+               (64, 8192, 128, S.X_F32), (65, 4096, 256, S.X_BF16), (300, 4096, 64, S.X_F32),
+               (1000, 2048, 100, S.X_BF16), (200, 1024, 256, S.X_BF16), (130, 256, 8, S.X_F32)]
+
+
+@pytest.mark.parametrize("T,H,E,xd", LOGIT_CASES)
+@pytest.mark.parametrize("data", ["normal", "wide"])
+def test_router_logits_bitexact(T, H, E, xd, data):
+    """moe_router_logits equals the oracle's pinned reduction order bit for bit.
+    'wide' scales every operand by 2^-12 .. 2^12, so the products of one
+    logit span 48 binades and nearly every partial sum rounds: a reduction
+    that differed from chained fmas in ascending k anywhere would show."""
+    rng = np.random.default_rng(T * 7 + H + E)
+    if data == "normal":
+        x32 = rng.standard_normal((T, H)).astype(np.float32)
+        wr = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    else:
+        x32 = (rng.standard_normal((T, H)) * np.exp2(rng.integers(-12, 13, (T, H)))).astype(np.float32)
+        wr = (rng.standard_normal((E, H)) * np.exp2(rng.integers(-12, 13, (E, H)) - 24.0)).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32)
+    if xd == S.X_F32:
+        x_h, x_d = x32, torch.from_numpy(x32).cuda()
+    else:
+        x_h = S.f32_to_bf16_bits(x32)
+        x_d = torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16)
+    cfg = B.make_config(T, H, 256, E, min(6, E), xd)
+    ws = torch.empty(B.moe_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(cfg, x_d, torch.from_numpy(wr).cuda(), torch.from_numpy(bias).cuda(), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x_h, wr, bias)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{(got != ref).sum()} logits differ"
+
+
 def _gpu_sort(ids_h, E, block_m):
     P = ids_h.size
     T = max(P, 1)
