@@ -668,126 +668,117 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Partial logits of large batches on the fp32 matrix cores. A 16x16x4 fp32
-// MFMA adds four products to each accumulator as four fused multiply-adds in
-// ascending k -- the chunk's chain (checked bit for bit against chained IEEE
-// fmas on the GPU over random operands of many magnitudes) -- at twice the
-// non-packed VALU rate, with its operands in registers. Chunks are whole LDS
-// stages of KS = 32 k (L % 32 == 0, so H % 2048 == 0; other widths take
-// router_partial_kernel). About 11% faster than the VALU kernel at 16,384
-// tokens; a stage still takes about 2.5x its MFMA time (stores, barriers
-// and operand reads between the MFMAs). Workgroup tile: 128 tokens x 64 experts over one
-// 8-chunk slice; wave w owns tokens 32w..32w+31 as 2 x 4 blocks of 16 x 16
-// (eight independent accumulator chains) and keeps the 3-level pairwise
-// stack of every output. Lane l supplies token row / expert column l % 16 at
-// k-quad element l / 16. x and Wr stay row-major in LDS (16-byte stores).
+// Partial logits of large batches on the fp32 matrix cores, fed straight from
+// memory. The 32x32x1 fp32 MFMA (two blocks) adds one product to each
+// accumulator per instruction, as an IEEE fused multiply-add (checked bit
+// for bit on the GPU), so issuing it in ascending k is the chunk's chain, at
+// twice the non-packed VALU rate. Each wave owns 64 tokens x 32 experts of
+// one 8-chunk slice: block b holds tokens 32b..32b+31, both blocks the same
+// 32 experts, so lane l supplies x row l and Wr row l % 32 -- 16 consecutive
+// k of each per batch, plain vector loads from L2 double-buffered in
+// registers: no LDS, no barriers. The 3-level pairwise stack of every output
+// sits beside the accumulators. Chunks are whole batches (L % 16 == 0:
+// H % 1024 == 0; other widths take router_partial_kernel). About 575 us at
+// 16,384 tokens and 150 us at 4,604 (the VALU kernel: 715 and 185); an LDS-
+// staged version with 16x16x4 MFMAs took 650 and 190 (barriers and stores
+// between the MFMAs).
 // ---------------------------------------------------------------------------
-template <typename XT, int KS>
+constexpr int RM_KB = 16;  // k per batch
+constexpr int RM_NBUF = 2;  // register sets: batch b + 2 is loaded while batch b runs (3 measured no faster)
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+template <typename XT>
+__device__ __forceinline__ void load16(const XT* p, float* o);
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(p)[i];
+    o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+  }
+}
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float* o) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      o[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+
+template <typename XT>
 __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
                                                              float* __restrict__ partial, int T, int H, int E) {
-  constexpr int TT = 128, TE = 64, RS = KS + 4;  // row stride: 16-byte aligned rows, reads spread over banks
-  constexpr int NX = TT * KS / 4 / 256, NWL = TE * KS / 4 / 256;  // float4 loads a thread
-  __shared__ __attribute__((aligned(16))) float xs[TT][RS];
-  __shared__ __attribute__((aligned(16))) float ws[TE][RS];
-  const int e0 = blockIdx.x * TE, t0 = blockIdx.y * TT, slice = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 15, kk = lane >> 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e0 = (blockIdx.x * 4 + wave) * 32, t0 = blockIdx.y * 64, slice = blockIdx.z;
   const int L = H >> 6;
-  const int kbeg = slice * NSLICE * L, kend = kbeg + NSLICE * L;
+  const int kbeg = slice * NSLICE * L, nb = NSLICE * L / RM_KB;  // batches in the slice (even)
+  const int t = t0 + lane, e = e0 + (lane & 31);
+  const bool tv = t < T, ev = e < E;
+  const XT* xrow = x + (size_t)(tv ? t : 0) * H + kbeg;
+  const float* wrow = wr + (size_t)(ev ? e : 0) * H + kbeg;
 
-  v4f acc[2][4], st0[2][4], st1[2][4], st2[2][4];
+  v32f acc = {}, st0 = {}, st1 = {}, st2 = {};
+  float xa[RM_NBUF][RM_KB], wb[RM_NBUF][RM_KB];
+  auto fetch = [&](int set, int b) {
+    b = b < nb ? b : nb - 1;  // past the end: re-read the last batch (branch-free)
+    load16<XT>(xrow + b * RM_KB, xa[set]);
+    load16<float>(wrow + b * RM_KB, wb[set]);
+    if (!tv) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = st0[a][b] = st1[a][b] = st2[a][b] = (v4f){};
-
-  float xr[NX][4], wrr[NWL][4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int n = 0; n < NX; ++n) {
-      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      xr[n][0] = xr[n][1] = xr[n][2] = xr[n][3] = 0.f;
-      if (t0 + r < T) load4<XT>(x + (size_t)(t0 + r) * H + k0 + kq, xr[n]);
+      for (int i = 0; i < RM_KB; ++i) xa[set][i] = 0.f;
     }
+    if (!ev) {
 #pragma unroll
-    for (int n = 0; n < NWL; ++n) {
-      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + r < E) v = *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + k0 + kq);
-      wrr[n][0] = v.x; wrr[n][1] = v.y; wrr[n][2] = v.z; wrr[n][3] = v.w;
+      for (int i = 0; i < RM_KB; ++i) wb[set][i] = 0.f;
     }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int n = 0; n < NX; ++n) {
-      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      *reinterpret_cast<float4*>(&xs[r][kq]) = make_float4(xr[n][0], xr[n][1], xr[n][2], xr[n][3]);
-    }
-#pragma unroll
-    for (int n = 0; n < NWL; ++n) {
-      const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      *reinterpret_cast<float4*>(&ws[r][kq]) = make_float4(wrr[n][0], wrr[n][1], wrr[n][2], wrr[n][3]);
-    }
-  };
-  auto quad = [&](int q) {
-    float a[2], b[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = xs[wave * 32 + i * 16 + m][4 * q + kk];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = ws[j * 16 + m][4 * q + kk];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   int chunk = 0, in_chunk = 0;
   auto push = [&]() {
     // chunk index within the slice as a 3-bit counter: the pairwise tree
-    // (element-wise selects: the sums of the VALU kernel's stack)
     const bool c0 = chunk & 1, c1 = chunk & 2, c2 = chunk & 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a0 = acc[i][j][v];
-          const float a1 = st0[i][j][v] + a0;  // level 1 (odd chunks)
-          const float a2 = st1[i][j][v] + a1;  // level 2 (chunks 3, 7)
-          const float a3 = st2[i][j][v] + a2;  // level 3 (chunk 7)
-          st0[i][j][v] = c0 ? st0[i][j][v] : a0;
-          st1[i][j][v] = (c0 && !c1) ? a1 : st1[i][j][v];
-          st2[i][j][v] = (c0 && c1) ? (c2 ? a3 : a2) : st2[i][j][v];
-          acc[i][j][v] = 0.f;
-        }
+    for (int v = 0; v < 32; ++v) {
+      const float a0 = acc[v];
+      const float a1 = st0[v] + a0;  // level 1 (odd chunks)
+      const float a2 = st1[v] + a1;  // level 2 (chunks 3, 7)
+      const float a3 = st2[v] + a2;  // level 3 (chunk 7)
+      st0[v] = c0 ? st0[v] : a0;
+      st1[v] = (c0 && !c1) ? a1 : st1[v];
+      st2[v] = (c0 && c1) ? (c2 ? a3 : a2) : st2[v];
+      acc[v] = 0.f;
+    }
     ++chunk;
   };
-
-  fetch(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += KS) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (k0 + KS < kend) fetch(k0 + KS);
-    // L % KS == 0 (the launch checks): a chunk ends only with a stage
+  auto batch = [&](int set, int b) {
 #pragma unroll
-    for (int q = 0; q < KS / 4; ++q) quad(q);
-    in_chunk += KS;
+    for (int i = 0; i < RM_KB; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xa[set][i], wb[set][i], acc, 0, 0, 0);
+    fetch(set, b + RM_NBUF);
+    in_chunk += RM_KB;
     if (in_chunk == L) {
       in_chunk = 0;
       push();
     }
+  };
+#pragma unroll
+  for (int i = 0; i < RM_NBUF; ++i) fetch(i, i);
+  for (int b = 0; b < nb; b += RM_NBUF) {
+#pragma unroll
+    for (int i = 0; i < RM_NBUF; ++i)
+      if (b + i < nb) batch(i, b + i);
   }
+  // block b = v / 16: token t0 + 32 b + 8 (vv / 4) + 4 (lane / 32) + vv % 4, expert e0 + lane % 32
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int t = t0 + wave * 32 + i * 16 + 4 * kk + v;
-        const int e = e0 + j * 16 + m;
-        if (t < T && e < E) partial[((size_t)slice * T + t) * E + e] = st2[i][j][v];
-      }
+  for (int v = 0; v < 32; ++v) {
+    const int vv = v & 15;
+    const int tt = t0 + 32 * (v >> 4) + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+    if (tt < T && ev) partial[((size_t)slice * T + tt) * E + e] = st2[v];
+  }
 }
 
 // logits[t][e] from the NS slice sums: one thread per (t, e).
@@ -825,11 +816,10 @@ hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, i
       router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
   } else {
     if (xq) return hipErrorInvalidValue;  // large batches quantize x in the top-k kernel
-    if ((H / 64) % 32 == 0) {
-      // stages of 32 k (64-k stages measured slower: more registers, the
-      // same per-stage overheads)
-      dim3 grid((E + 63) / 64, (T + 127) / 128, NSLICE);
-      router_mfma_kernel<XT, 32><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
+    if ((H / 64) % RM_KB == 0) {
+      // four waves a workgroup, each 64 tokens x 32 experts
+      dim3 grid((E + 127) / 128, (T + 63) / 64, NSLICE);
+      router_mfma_kernel<XT><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E);
     } else {
       dim3 grid((E + 63) / 64, (T + 63) / 64, NSLICE);
       router_partial_kernel<XT, 4, 4, 32, 8><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, 0, nullptr, nullptr);
