@@ -740,19 +740,20 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const XT* __restric
   };
   int chunk = 0, in_chunk = 0;
   auto push = [&]() {
-    // chunk index within the slice as a 3-bit counter: the pairwise tree
-    const bool c0 = chunk & 1, c1 = chunk & 2, c2 = chunk & 4;
-#pragma unroll
-    for (int v = 0; v < 32; ++v) {
-      const float a0 = acc[v];
-      const float a1 = st0[v] + a0;  // level 1 (odd chunks)
-      const float a2 = st1[v] + a1;  // level 2 (chunks 3, 7)
-      const float a3 = st2[v] + a2;  // level 3 (chunk 7)
-      st0[v] = c0 ? st0[v] : a0;
-      st1[v] = (c0 && !c1) ? a1 : st1[v];
-      st2[v] = (c0 && c1) ? (c2 ? a3 : a2) : st2[v];
-      acc[v] = 0.f;
+    // chunk index within the slice as a 3-bit counter (wave-uniform): the
+    // pairwise tree, only the adds this chunk needs
+    if (!(chunk & 1)) {
+      st0 = acc;
+    } else {
+      const v32f a1 = st0 + acc;  // level 1
+      if (!(chunk & 2)) {
+        st1 = a1;
+      } else {
+        const v32f a2 = st1 + a1;  // level 2
+        st2 = (chunk & 4) ? st2 + a2 : a2;  // level 3 at chunk 7
+      }
     }
+    acc = (v32f){};
     ++chunk;
   };
   auto batch = [&](int set, int b) {
