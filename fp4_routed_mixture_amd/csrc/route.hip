@@ -6,9 +6,11 @@
 // from 0; the 64 chunk sums are added as a perfect pairwise tree in index
 // order; the bias is added last.
 //
-// router_partial: the 64 chunks form 8 slices of 8 chunks. A workgroup
-// computes a (tokens x experts) tile over one slice, staging both operands
-// through LDS; each thread owns an RA x RB block of outputs and keeps a
+// Large batches: the 64 chunks form 8 slices of 8 chunks. router_mfma (H a
+// multiple of 1024) runs each output's chain on fp32 matrix cores, one fused
+// multiply-add per 32x32x1 MFMA in ascending k; router_partial (other H)
+// on the VALU, a workgroup staging a (tokens x experts) tile's operands
+// through LDS, each thread owning an RA x RB block of outputs. Both keep a
 // 3-level pairwise stack per output, pushing a chunk sum whenever a chunk
 // ends (the carry chain of a binary counter reproduces the tree exactly).
 // The slice sums (tree level 3) go to partial[8][T][E]; the kernels below add
