@@ -147,13 +147,12 @@ hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, in
   const size_t lds = (size_t)(H + H / 64) * 4;
   // above 64 KB of dynamic LDS a kernel must opt in; static LDS (r_sh) counts
   // against the same 160 KB, so ask for what H <= 16384 needs
-  static bool lds_opt_in = false;
-  if (!lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute((const void*)combine_residual_norm_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (16384 + 256) * 4);
-    if (e != hipSuccess) return e;
-    lds_opt_in = true;
-  }
+  static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
+  const hipError_t e = moe::once_per_device(lds_opt_in, [] {
+    return hipFuncSetAttribute((const void*)combine_residual_norm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (16384 + 256) * 4);
+  });
+  if (e != hipSuccess) return e;
   const int threads = H / 4 < 1024 ? H / 4 : 1024;  // H % 256 == 0: whole waves
   combine_residual_norm_kernel<<<T, threads, lds, st>>>(y, w, H, K, x, layer_out, xn);
   return hipGetLastError();

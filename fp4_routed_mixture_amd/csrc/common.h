@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -11,6 +13,23 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #define MOE_WAVE 64
 
 namespace moe {
+
+// Host: run set() once for each device it is called on (the attributes that
+// let a kernel use more than 64 KB of LDS belong to the device current when
+// they are set). done: one flag per device id. Concurrent first calls on a
+// device may both run set(), which only repeats the same settings.
+constexpr int kMaxDevices = 64;
+template <typename F>
+inline hipError_t once_per_device(std::atomic<bool>* done, F set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = set();
+  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 // ---------------------------------------------------------------------------
 // fp32 exp and sigmoid built from IEEE operations only, so the same bits come

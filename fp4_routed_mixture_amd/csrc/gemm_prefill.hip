@@ -394,16 +394,16 @@ hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc
   const size_t lds = std::max<size_t>((size_t)BM * (K / 128 + 1) * 4, gate_up ? 0 : (size_t)NWAVE * 32 * 36 * 4);
   // above 64 KB of dynamic LDS a kernel must opt in; the static arrays
   // (pair-row stages, row maps) share the 160 KB
-  static bool lds_opt_in = false;
-  if (!lds_opt_in) {
+  static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
+  const hipError_t e = moe::once_per_device(lds_opt_in, [] {
     const int cap = 160 * 1024 - 4 * B_STAGE - 2 * BM * 4 - 1024;
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<true>,
+    hipError_t r = hipFuncSetAttribute((const void*)prefill_gemm_kernel<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)prefill_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-    if (e != hipSuccess) return e;
-    lds_opt_in = true;
-  }
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)prefill_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+    return r;
+  });
+  if (e != hipSuccess) return e;
   if (gate_up)
     prefill_gemm_kernel<true><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles, K,
                                                     NT, top_k, P, rows_are_tokens, aq, as, y, out_n);

@@ -895,13 +895,12 @@ hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T
   if (T <= 0) return hipSuccess;
   if (T * K > moe::SB || K > 16 || E > 1024 || T * E > RS_MAX_TE) return hipErrorInvalidValue;
   // above 64 KB of LDS a kernel must opt in (gfx950: 160 KB per workgroup)
-  static bool lds_opt_in = false;
-  if (!lds_opt_in) {
-    hipError_t e = hipFuncSetAttribute((const void*)route_sort_small_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    if (e != hipSuccess) return e;
-    lds_opt_in = true;
-  }
+  static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
+  const hipError_t e = moe::once_per_device(lds_opt_in, [] {
+    return hipFuncSetAttribute((const void*)route_sort_small_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               150 * 1024);
+  });
+  if (e != hipSuccess) return e;
   const int P = T * K, W = (P + 31) / 32;
   const size_t lds = (size_t)(std::max(T * E, E * W) + E + E + 1 + 1024) * 4;
   route_sort_small_kernel<<<1, 1024, lds, st>>>(partial, bias, T, E, K, block_m, ids, w, counts, offsets, sorted, pos,

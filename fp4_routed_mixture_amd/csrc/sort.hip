@@ -197,19 +197,17 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
                       int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
                       hipStream_t st) {
   // gfx950 has 160 KB of LDS per workgroup; above 64 KB a kernel must opt in
-  static bool lds_opt_in = false;
-  if (!lds_opt_in) {
+  static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
+  const hipError_t eo = moe::once_per_device(lds_opt_in, [] {
     hipError_t e1 = hipFuncSetAttribute((const void*)sort_small_kernel,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     hipError_t e2 = hipFuncSetAttribute((const void*)sort_count_kernel,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     hipError_t e3 = hipFuncSetAttribute((const void*)sort_scan_kernel<true>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScanLdsMax);
-    if (e1 != hipSuccess) return e1;
-    if (e2 != hipSuccess) return e2;
-    if (e3 != hipSuccess) return e3;
-    lds_opt_in = true;
-  }
+    return e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
+  });
+  if (eo != hipSuccess) return eo;
   if (P <= moe::SB) {
     size_t lds = (size_t)(E * ((P + 31) / 32) + E + E + 1 + 1024) * 4;
     sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles);
