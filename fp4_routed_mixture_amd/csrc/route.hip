@@ -7,8 +7,8 @@
 // order; the bias is added last.
 //
 // Large batches: the 64 chunks form 8 slices of 8 chunks. router_mfma (H a
-// multiple of 1024) runs each output's chain on fp32 matrix cores, one fused
-// multiply-add per 32x32x1 MFMA in ascending k; router_partial (other H)
+// multiple of 1024) runs each output's chain on fp32 matrix cores, two fused
+// multiply-adds per 32x32x2 MFMA in ascending k; router_partial (other H)
 // on the VALU, a workgroup staging a (tokens x experts) tile's operands
 // through LDS, each thread owning an RA x RB block of outputs. Both keep a
 // 3-level pairwise stack per output, pushing a chunk sum whenever a chunk
@@ -671,117 +671,144 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
 
 // ---------------------------------------------------------------------------
 // Partial logits of large batches on the fp32 matrix cores, fed straight from
-// memory. The 32x32x1 fp32 MFMA (two blocks) adds one product to each
-// accumulator per instruction, as an IEEE fused multiply-add (checked bit
-// for bit on the GPU), so issuing it in ascending k is the chunk's chain, at
-// twice the non-packed VALU rate. Each wave owns 64 tokens x 32 experts of
-// one 8-chunk slice: block b holds tokens 32b..32b+31, both blocks the same
-// 32 experts, so lane l supplies x row l and Wr row l % 32 -- 16 consecutive
-// k of each per batch, plain vector loads from L2 double-buffered in
-// registers: no LDS, no barriers. The 3-level pairwise stack of every output
-// sits beside the accumulators. Chunks are whole batches (L % 16 == 0:
-// H % 1024 == 0; other widths take router_partial_kernel). About 575 us at
-// 16,384 tokens and 150 us at 4,604 (the VALU kernel: 715 and 185); an LDS-
-// staged version with 16x16x4 MFMAs took 650 and 190 (barriers and stores
-// between the MFMAs).
+// memory. The 32x32x2 fp32 MFMA adds two products to each accumulator per
+// instruction as two chained IEEE fused multiply-adds, k slot 0 then slot 1
+// (checked bit for bit on the GPU), so issuing it over ascending k pairs is
+// the chunk's chain, at twice the non-packed VALU rate. Each wave owns 64
+// tokens x 32 experts of one 8-chunk slice as two accumulators (token blocks
+// 0..31 and 32..63: two independent chains a wave) plus the 3-level pairwise
+// stack of every output. Lanes l and l + 32 read the two halves of the same
+// row's 16-k batch (8 consecutive k each), so one load touches 32 cache lines
+// and no lane re-reads what its partner holds; a v_permlane32_swap per
+// register pair then puts k 2m in the low half and k 2m + 1 in the high half
+// of one register, the MFMA's k slots. Plain vector loads from L2, double-
+// buffered in registers: no LDS, no barriers. Chunks are whole batches
+// (L % 16 == 0: H % 1024 == 0; other widths take router_partial_kernel).
 // ---------------------------------------------------------------------------
-constexpr int RM_KB = 16;  // k per batch
-constexpr int RM_NBUF = 2;  // register sets: batch b + 2 is loaded while batch b runs (3 measured no faster)
-typedef float v32f __attribute__((ext_vector_type(32)));
+constexpr int RM_KB = 16;  // k per batch (32 measured no faster)
+constexpr int RM_NBUF = 2;  // register sets: batch b + 2 is loaded while batch b runs
 
-template <typename XT>
-__device__ __forceinline__ void load16(const XT* p, float* o);
-template <>
-__device__ __forceinline__ void load16<float>(const float* p, float* o) {
+// NV consecutive values as fp32 (16-byte aligned, NV % 8 == 0).
+template <typename XT, int NV>
+__device__ __forceinline__ void load_row(const XT* p, float* o) {
+  if constexpr (sizeof(XT) == 4) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = reinterpret_cast<const float4*>(p)[i];
-    o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+    for (int i = 0; i < NV / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(p)[i];
+      o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV / 8; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        o[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
   }
 }
-template <>
-__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float* o) {
+
+// In: lane half h holds k NV h + i of the batch in r[i]. Out: r[2m] holds k 2m
+// (low half) and 2m + 1 (high half), r[2m + 1] holds k NV + 2m and NV + 2m + 1:
+// the swap exchanges the high half of r[2m] with the low half of r[2m + 1].
+template <int NV>
+__device__ __forceinline__ void pair_k(float* r) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-      o[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-    }
+  for (int m = 0; m < NV / 2; ++m) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(r[2 * m]), __float_as_uint(r[2 * m + 1]), false,
+                                                    false);
+    r[2 * m] = __uint_as_float(s[0]);
+    r[2 * m + 1] = __uint_as_float(s[1]);
   }
 }
 
 template <typename XT>
 __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const XT* __restrict__ x, const float* __restrict__ wr,
                                                              float* __restrict__ partial, int T, int H, int E) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int KB = RM_KB, NV = KB / 2;  // NV: values a lane loads per row and batch
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
   const int e0 = (blockIdx.x * 4 + wave) * 32, t0 = blockIdx.y * 64, slice = blockIdx.z;
   const int L = H >> 6;
-  const int kbeg = slice * NSLICE * L, nb = NSLICE * L / RM_KB;  // batches in the slice (even)
-  const int t = t0 + lane, e = e0 + (lane & 31);
-  const bool tv = t < T, ev = e < E;
-  const XT* xrow = x + (size_t)(tv ? t : 0) * H + kbeg;
-  const float* wrow = wr + (size_t)(ev ? e : 0) * H + kbeg;
+  const int kbeg = slice * NSLICE * L, nb = NSLICE * L / KB;  // batches in the slice (even)
+  const int e = e0 + r;
+  const bool ev = e < E;
+  // Rows past T or E read row 0 instead: an MFMA output depends only on its
+  // own A row and B column, and those outputs are not stored.
+  const int ta = t0 + r < T ? t0 + r : 0, tb = t0 + 32 + r < T ? t0 + 32 + r : 0;
+  const XT* xr0 = x + (size_t)ta * H + kbeg + NV * h;
+  const XT* xr1 = x + (size_t)tb * H + kbeg + NV * h;
+  const float* wrow = wr + (size_t)(ev ? e : 0) * H + kbeg + NV * h;
 
-  v32f acc = {}, st0 = {}, st1 = {}, st2 = {};
-  float xa[RM_NBUF][RM_KB], wb[RM_NBUF][RM_KB];
+  v16f acc[2] = {}, st0[2] = {}, st1[2] = {}, st2[2] = {};
+  float xa[RM_NBUF][2][NV], wb[RM_NBUF][NV];
   auto fetch = [&](int set, int b) {
     b = b < nb ? b : nb - 1;  // past the end: re-read the last batch (branch-free)
-    load16<XT>(xrow + b * RM_KB, xa[set]);
-    load16<float>(wrow + b * RM_KB, wb[set]);
-    if (!tv) {
-#pragma unroll
-      for (int i = 0; i < RM_KB; ++i) xa[set][i] = 0.f;
-    }
-    if (!ev) {
-#pragma unroll
-      for (int i = 0; i < RM_KB; ++i) wb[set][i] = 0.f;
-    }
+    load_row<XT, NV>(xr0 + b * KB, xa[set][0]);
+    load_row<XT, NV>(xr1 + b * KB, xa[set][1]);
+    load_row<float, NV>(wrow + b * KB, wb[set]);
   };
   int chunk = 0, in_chunk = 0;
   auto push = [&]() {
     // chunk index within the slice as a 3-bit counter (wave-uniform): the
     // pairwise tree, only the adds this chunk needs
-    if (!(chunk & 1)) {
-      st0 = acc;
-    } else {
-      const v32f a1 = st0 + acc;  // level 1
-      if (!(chunk & 2)) {
-        st1 = a1;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (!(chunk & 1)) {
+        st0[blk] = acc[blk];
       } else {
-        const v32f a2 = st1 + a1;  // level 2
-        st2 = (chunk & 4) ? st2 + a2 : a2;  // level 3 at chunk 7
+        const v16f a1 = st0[blk] + acc[blk];  // level 1
+        if (!(chunk & 2)) {
+          st1[blk] = a1;
+        } else {
+          const v16f a2 = st1[blk] + a1;  // level 2
+          st2[blk] = (chunk & 4) ? st2[blk] + a2 : a2;  // level 3 at chunk 7
+        }
       }
+      acc[blk] = (v16f){};
     }
-    acc = (v32f){};
     ++chunk;
   };
   auto batch = [&](int set, int b) {
+    pair_k<NV>(xa[set][0]);
+    pair_k<NV>(xa[set][1]);
+    pair_k<NV>(wb[set]);
 #pragma unroll
-    for (int i = 0; i < RM_KB; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xa[set][i], wb[set][i], acc, 0, 0, 0);
+    for (int s = 0; s < NV; ++s) {
+      const int reg = s < NV / 2 ? 2 * s : 2 * (s - NV / 2) + 1;  // k 2s, 2s + 1
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[set][0][reg], wb[set][reg], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[set][1][reg], wb[set][reg], acc[1], 0, 0, 0);
+    }
     fetch(set, b + RM_NBUF);
-    in_chunk += RM_KB;
+    in_chunk += KB;
     if (in_chunk == L) {
       in_chunk = 0;
       push();
     }
   };
+  // Sets are issued in the order the loop consumes them, here as on the loop's
+  // back edge, so that the wait before a set's first use counts only that
+  // set's loads (with the prologue's loads in another order the waits at the
+  // loop head covered both sets).
 #pragma unroll
-  for (int i = 0; i < RM_NBUF; ++i) fetch(i, i);
-  for (int b = 0; b < nb; b += RM_NBUF) {
-#pragma unroll
-    for (int i = 0; i < RM_NBUF; ++i)
-      if (b + i < nb) batch(i, b + i);
+  for (int i = 0; i < RM_NBUF; ++i) {
+    fetch(i, i);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // block b = v / 16: token t0 + 32 b + 8 (vv / 4) + 4 (lane / 32) + vv % 4, expert e0 + lane % 32
+  for (int b = 0; b < nb; b += RM_NBUF) {  // nb % RM_NBUF == 0: every pass runs every set
 #pragma unroll
-  for (int v = 0; v < 32; ++v) {
-    const int vv = v & 15;
-    const int tt = t0 + 32 * (v >> 4) + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
-    if (tt < T && ev) partial[((size_t)slice * T + tt) * E + e] = st2[v];
+    for (int i = 0; i < RM_NBUF; ++i) batch(i, b + i);
   }
+  // block blk: token t0 + 32 blk + 8 (v / 4) + 4 (lane / 32) + v % 4, expert e0 + lane % 32
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tt = t0 + 32 * blk + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (tt < T && ev) partial[((size_t)slice * T + tt) * E + e] = st2[blk][v];
+    }
 }
 
 // logits[t][e] from the NS slice sums: one thread per (t, e).
