@@ -31,6 +31,8 @@
 // sums; topk_quant uses one wave per token.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "sort_dev.h"
@@ -836,14 +838,21 @@ hipError_t launch_partial(const XT* x, const float* wr, float* partial, int T, i
   } else if (ns == NSLICE_SMALL) {
     // one chunk per workgroup, one LDS stage (64 k) per chunk sub-range; with
     // xq, slices 64.. quantize x (one token row per workgroup)
-    const int ex = (E + 15) / 16;
-    dim3 grid(ex, 1, NSLICE_SMALL + (xq ? (T + ex - 1) / ex : 0));
-    if (T <= 16)
-      router_partial_kernel<XT, 1, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
-    else if (T <= 32)
-      router_partial_kernel<XT, 2, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
-    else
-      router_partial_kernel<XT, 4, 1, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    auto go = [&](auto ra, auto rb) {
+      constexpr int RA = decltype(ra)::value, RB = decltype(rb)::value;
+      const int ex = (E + 16 * RB - 1) / (16 * RB);
+      dim3 grid(ex, 1, NSLICE_SMALL + (xq ? (T + ex - 1) / ex : 0));
+      router_partial_kernel<XT, RA, RB, 64, 1><<<grid, 256, 0, st>>>(x, wr, partial, T, H, E, mx, xq, xs);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    // above 32 tokens 64 x 32 tiles (8 outputs a thread, fewer LDS bytes per
+    // fma): 10.4 -> 8.9 us at 64 tokens; 64 x 64 spills, and 32 x 32 tiles
+    // at 17..32 tokens measured no faster than 32 x 16
+    if (T <= 16) go(I1{}, I1{});
+    else if (T <= 32) go(I2{}, I1{});
+    else go(I4{}, I2{});
   } else {
     if (xq) return hipErrorInvalidValue;  // large batches quantize x in the top-k kernel
     if ((H / 64) % RM_KB == 0) {
