@@ -222,44 +222,73 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
 #pragma unroll
     for (int b = 0; b < RB; ++b) { acc[a][b] = 0.f; st0[a][b] = 0.f; st1[a][b] = 0.f; st2[a][b] = 0.f; }
 
-  float xr[NX][4], wrr[NW][4];
-  auto fetch = [&](int k0) {
+  // Register sets of fetched stages: D = 1 fetches the next stage while the
+  // current one runs; the four-chunk tiny-batch slices (a multiple of four
+  // stages: 4 L with L % 64 == 0) have four stages in flight at once, since
+  // a stage computes for less than a memory latency.
+  constexpr int D = CPS == 4 ? 4 : 1;
+  // Raw bits in registers, converted to fp32 at the LDS store: a conversion
+  // right after the load (or a load under a branch) makes the compiler wait
+  // for it at once, and the prefetch would not overlap anything. Rows past T
+  // or E read row 0: their outputs are never stored.
+  using Raw = std::conditional_t<sizeof(XT) == 2, uint2, float4>;
+  Raw xr[D][NX];
+  float4 wrr[D][NW];
+  auto fetch = [&](int set, int k0) {
 #pragma unroll
     for (int n = 0; n < NX; ++n) {
       const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      xr[n][0] = xr[n][1] = xr[n][2] = xr[n][3] = 0.f;
-      if (t0 + r < T) load4<XT>(x + (size_t)(t0 + r) * H + k0 + kq, xr[n]);
+      const int row = t0 + r < T ? t0 + r : 0;
+      xr[set][n] = *reinterpret_cast<const Raw*>(x + (size_t)row * H + k0 + kq);
     }
 #pragma unroll
     for (int n = 0; n < NW; ++n) {
       const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + r < E) v = *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * H + k0 + kq);
-      wrr[n][0] = v.x; wrr[n][1] = v.y; wrr[n][2] = v.z; wrr[n][3] = v.w;
+      const int row = e0 + r < E ? e0 + r : 0;
+      wrr[set][n] = *reinterpret_cast<const float4*>(wr + (size_t)row * H + k0 + kq);
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int set) {
 #pragma unroll
     for (int n = 0; n < NX; ++n) {
       const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
+      float v[4];
+      if constexpr (sizeof(XT) == 2) {
+        const uint2 b = xr[set][n];
+        v[0] = __uint_as_float(b.x << 16);
+        v[1] = __uint_as_float(b.x & 0xffff0000u);
+        v[2] = __uint_as_float(b.y << 16);
+        v[3] = __uint_as_float(b.y & 0xffff0000u);
+      } else {
+        v[0] = xr[set][n].x; v[1] = xr[set][n].y; v[2] = xr[set][n].z; v[3] = xr[set][n].w;
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) xs[kq + u][r] = xr[n][u];
+      for (int u = 0; u < 4; ++u) xs[kq + u][r] = v[u];
     }
 #pragma unroll
     for (int n = 0; n < NW; ++n) {
       const int g = tid + n * 256, r = g / (KS / 4), kq = (g % (KS / 4)) * 4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ws[kq + u][r] = wrr[n][u];
+      ws[kq + 0][r] = wrr[set][n].x;
+      ws[kq + 1][r] = wrr[set][n].y;
+      ws[kq + 2][r] = wrr[set][n].z;
+      ws[kq + 3][r] = wrr[set][n].w;
     }
   };
 
   int chunk = 0, in_chunk = 0;
-  fetch(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += KS) {
+  if constexpr (D == 1) fetch(0, kbeg);
+  else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) fetch(i, kbeg + i * KS);  // kend - kbeg >= D KS
+  }
+  for (int k0 = kbeg; k0 < kend; k0 += D * KS) {
+#pragma unroll
+   for (int i = 0; i < D; ++i) {
+    const int ks = k0 + i * KS;  // this stage
     __syncthreads();
-    stash();
+    stash(i);
     __syncthreads();
-    if (k0 + KS < kend) fetch(k0 + KS);
+    if (ks + D * KS < kend) fetch(i, ks + D * KS);  // the stage D ahead
     // Four k per group (L % 4 == 0, so a chunk never ends inside a group):
     // the group's LDS reads are issued together, then its fmas run in
     // ascending k per output. Where L is a multiple of KS (the one-chunk
@@ -350,6 +379,7 @@ __global__ __launch_bounds__(256, 4) void router_partial_kernel(const XT* __rest
         }
       }
     }
+   }
   }
 #pragma unroll
   for (int a = 0; a < RA; ++a) {
