@@ -145,22 +145,29 @@ __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
     const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ a, int I) {
   __shared__ float red[NW][2][16][64];
   const int j = blockIdx.x, q = blockIdx.y;
-  if (q >= *n_tiles) return;
-  const int e = tile_expert[q];
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, part = c >> 4;
+  // The tile count, the tile's expert and its pair ids are loaded together
+  // (q < max_tiles: within both arrays, whose entries past n_tiles are never
+  // used), and the pair row's scale before the main loop: every index load
+  // waited for in turn would delay the start of the weight stream.
+  const int nt = *n_tiles;
+  const int e = tile_expert[q];
   const int pair = sorted[q * DM + (c & 15)];
+  // (an empty asm reading the three values: otherwise the compiler sinks the
+  // second and third load below the exit test and waits for each in turn)
+  asm volatile("" ::"s"(nt), "s"(e), "v"(pair));
+  if (q >= nt) return;
   const bool valid = pair < P;
   const int row = valid ? pair / top_k : 0;
+  const float s = xs[row];
   decode_mainloop<2, true>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
 
-  // a = (g * sigmoid(g)) * u for the hi-column lanes' rows
-  const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
-  if ((l & 31) >= 16) return;
+  // a = (g * sigmoid(g)) * u for the hi-column lanes' rows (lane l: sort row
+  // q DM + l % 16, the pair loaded above)
+  const int l = lane, vq = threadIdx.x >> 6;
+  if ((l & 31) >= 16 || !valid) return;
   const int op = q * DM + (l & 15);
-  const int opair = sorted[op];
-  if (opair >= P) return;
-  const float s = xs[opair / top_k];
   float* arow = a + (size_t)op * I + j * 32;
 #pragma unroll
   for (int vv = 0; vv < 4; ++vv) {
@@ -176,21 +183,22 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
     const int32_t* __restrict__ n_tiles, int K, int NT, int top_k, int P, float* __restrict__ y, int H) {
   __shared__ float red[NW][2][16][64];
   const int j = blockIdx.x, q = blockIdx.y;  // j: pair of row tiles 2j, 2j+1
-  if (q >= *n_tiles) return;
-  const int e = tile_expert[q];
   const int lane = threadIdx.x & 63;
   const int c = lane & 31, part = c >> 4;
   const int p = q * DM + (c & 15);
-  const bool valid = sorted[p] < P;
+  // loaded together, as in the gate/up kernel (q < max_tiles, p < capacity)
+  const int nt = *n_tiles;
+  const int e = tile_expert[q];
+  const int pair = sorted[p];
+  const float s = as[p];
+  asm volatile("" ::"s"(nt), "s"(e), "v"(pair), "v"(s));
+  if (q >= nt) return;
+  const bool valid = pair < P;
   decode_mainloop<2, false>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
 
-  const int l = threadIdx.x & 63, vq = threadIdx.x >> 6;
-  if ((l & 31) >= 16) return;
-  const int op = q * DM + (l & 15);
-  const int opair = sorted[op];
-  if (opair >= P) return;
-  const float s = as[op];
-  float* yrow = y + (size_t)opair * H + j * 64;
+  const int l = lane, vq = threadIdx.x >> 6;
+  if ((l & 31) >= 16 || !valid) return;  // lane l: sort row p, its pair above
+  float* yrow = y + (size_t)pair * H + j * 64;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll

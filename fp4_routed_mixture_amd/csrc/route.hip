@@ -412,10 +412,14 @@ __device__ __forceinline__ float finish_logit(const float* __restrict__ partial,
                                               int E, int t, int e) {
   float v[NS];
   const size_t st = (size_t)T * E, o = (size_t)t * E + e;
+  // read through a pointer that is never null (partial stands in, unused,
+  // when there is no bias), so the load needs no branch of its own and can
+  // go out with the slice sums
+  const float b = (bias ? bias : partial)[e];
 #pragma unroll
   for (int i = 0; i < NS; ++i) v[i] = partial[i * st + o];
   const float l = tree_sum<NS>(v);
-  return bias ? l + bias[e] : l;
+  return bias ? l + b : l;
 }
 
 // Wave-wide max / min of a uint32 by DPP: row shifts build each 16-lane
@@ -627,10 +631,11 @@ template <int NI>
 __device__ __forceinline__ void score_items(const float* __restrict__ partial, const float* __restrict__ bias, int TE,
                                             int E, float* sc) {
   const int tid = threadIdx.x;
-  float v[NI][NSLICE_TINY];
+  float v[NI][NSLICE_TINY], b[NI];
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
     const int ic = min(u * 1024 + tid, TE - 1);
+    b[u] = (bias ? bias : partial)[ic % E];  // pointer never null, as in finish_logit
 #pragma unroll
     for (int sl = 0; sl < NSLICE_TINY; ++sl) v[u][sl] = partial[(size_t)sl * TE + ic];
   }
@@ -639,7 +644,7 @@ __device__ __forceinline__ void score_items(const float* __restrict__ partial, c
     const int i = u * 1024 + tid;
     if (i < TE) {
       const float l = tree_sum<NSLICE_TINY>(v[u]);
-      sc[i] = moe::sigmoid_fixed(bias ? l + bias[i % E] : l);
+      sc[i] = moe::sigmoid_fixed(bias ? l + b[u] : l);
     }
   }
 }
