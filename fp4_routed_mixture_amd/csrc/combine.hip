@@ -12,21 +12,31 @@
 
 namespace {
 
+// One instance per top-k K: every slot's weight and y column are loaded
+// before the first fma, so a column waits for memory once rather than once a
+// slot (with a runtime K the loads sat under branches, each waited for alone).
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w, int T,
-                                                      int H, int K, float* __restrict__ out) {
+                                                      int H, float* __restrict__ out) {
   const size_t n4 = (size_t)T * (H >> 2);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
     const size_t t = i / (H >> 2);
     const int n = (int)(i - t * (H >> 2)) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wj[K];
+    v4f v[K];
+#pragma unroll
     for (int j = 0; j < K; ++j) {
-      const float wj = w[t * K + j];
+      wj[j] = w[t * K + j];
       // y is read exactly once: keep it out of the caches
-      const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + (t * K + j) * (size_t)H + n));
-      acc.x = __builtin_fmaf(wj, v[0], acc.x);
-      acc.y = __builtin_fmaf(wj, v[1], acc.y);
-      acc.z = __builtin_fmaf(wj, v[2], acc.z);
-      acc.w = __builtin_fmaf(wj, v[3], acc.w);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + (t * K + j) * (size_t)H + n));
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      acc.x = __builtin_fmaf(wj[j], v[j][0], acc.x);
+      acc.y = __builtin_fmaf(wj[j], v[j][1], acc.y);
+      acc.z = __builtin_fmaf(wj[j], v[j][2], acc.z);
+      acc.w = __builtin_fmaf(wj[j], v[j][3], acc.w);
     }
     *reinterpret_cast<float4*>(out + t * H + n) = acc;
   }
@@ -121,12 +131,22 @@ int grid_for(size_t n) {
   return (int)(b < 65536 ? (b ? b : 1) : 65536);
 }
 
+// The combine instance for top-k K (1..16).
+template <int KK>
+hipError_t launch_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st) {
+  if (K == KK) {
+    combine_kernel<KK><<<grid_for((size_t)T * (H >> 2)), 256, 0, st>>>(y, w, T, H, out);
+    return hipGetLastError();
+  }
+  if constexpr (KK < 16) return launch_combine<KK + 1>(y, w, T, H, K, out, st);
+  else return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t moe_k_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  combine_kernel<<<grid_for((size_t)T * (H >> 2)), 256, 0, st>>>(y, w, T, H, K, out);
-  return hipGetLastError();
+  return launch_combine<1>(y, w, T, H, K, out, st);
 }
 
 hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t st) {
