@@ -147,3 +147,15 @@ def test_single_expert_k1_is_dense_mlp_on_gpu():
     o = oracle_layer(w, S.activations(w))
     assert np.all(g["ids"] == 0) and np.all(g["w"] == 1.0)
     assert np.array_equal(g["out"], o["out"])
+
+
+@pytest.mark.parametrize("k", list(range(1, 17)))
+def test_forward_every_top_k(k):
+    """Each top-k from 1 to 16 (the combine has one kernel instance per k):
+    a small int8 layer equals the oracle bit for bit, routing and output."""
+    w = S.Workload(f"topk{k}", 5, 256, 128, 16, k, S.X_BF16, S.ACT_INT8, False, 100 + k)
+    print(f"[every top-k] {S.describe(w)}", flush=True)
+    g = run_forward(w, SD.load_layer(w), SD.activations(w))
+    o = oracle_layer(w, S.activations(w))
+    assert np.array_equal(g["ids"], o["ids"])
+    assert np.array_equal(g["out"], o["out"])
