@@ -110,7 +110,8 @@ def test_router_kernels_agree(T):
 # the VALU (other H); E not a multiple of a tile included.
 LOGIT_CASES = [(4, 4096, 256, S.X_BF16), (16, 4096, 256, S.X_F32), (17, 4096, 256, S.X_BF16),
                (64, 8192, 128, S.X_F32), (65, 4096, 256, S.X_BF16), (300, 4096, 64, S.X_F32),
-               (1000, 2048, 100, S.X_BF16), (200, 1024, 256, S.X_BF16), (130, 256, 8, S.X_F32)]
+               (1000, 2048, 100, S.X_BF16), (200, 1024, 256, S.X_BF16), (130, 256, 8, S.X_F32),
+               (600, 2304, 96, S.X_BF16), (48, 1280, 40, S.X_F32)]
 
 
 @pytest.mark.parametrize("T,H,E,xd", LOGIT_CASES)
