@@ -70,13 +70,15 @@ __device__ inline void write_tiles_and_padding(const int* counts, const int* off
                                                int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
                                                int32_t* __restrict__ n_tiles) {
   const int tid = threadIdx.x;
-  // padding slots: (expert, slot) items spread over the threads, so the slots
-  // of one expert go to consecutive threads
+  // padding slots: g = blockDim.x / E threads per expert (E <= blockDim.x)
+  // stride over that expert's padding [offs + count, offs[e + 1]) only: one
+  // division per thread rather than one per (expert, slot) candidate
   if (block_m > 1) {
-    const int per = block_m - 1;
-    for (int i = tid; i < E * per; i += blockDim.x) {
-      const int e = i / per, p = offs[e] + counts[e] + (i - e * per);
-      if (p < offs[e + 1]) sorted[p] = P;
+    const int g = (int)blockDim.x / E;
+    if (tid < g * E) {
+      const int e = tid / g;
+      const int end = offs[e + 1];
+      for (int p = offs[e] + counts[e] + (tid - e * g); p < end; p += g) sorted[p] = P;
     }
   }
   for (int e = tid; e < E; e += blockDim.x)
