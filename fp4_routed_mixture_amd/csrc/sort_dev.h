@@ -37,27 +37,31 @@ __device__ inline void block_rank(int my_id, bool my_valid, int n, int E, uint32
   __syncthreads();
 }
 
+// Inclusive prefix sum over a wave by DPP, in registers: row shifts 1, 2, 4, 8
+// scan each 16-lane row (a lane without a source adds 0), then the row
+// broadcasts of lanes 15 and 31 carry the row totals into the later rows.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Block-wide exclusive scan of padded counts over E experts (E <= 1024,
-// blockDim.x == 1024): writes offsets[0..E]. A scan inside each wave
-// (shuffles), the wave totals scanned by wave 0, then one add: two barriers.
+// blockDim.x == 1024): writes offsets[0..E]. A scan inside each wave, the
+// wave totals scanned by wave 0, then one add: two barriers.
 __device__ inline void scan_offsets(const int* counts_lds, int E, int block_m, int* offs_lds, int* tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int v = 0;
   if (tid < E) v = (counts_lds[tid] + block_m - 1) / block_m * block_m;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = v;  // inclusive wave totals
   __syncthreads();
   if (wave == 0) {
-    int t = lane < 16 ? tmp[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int n = __shfl_up(t, o, 64);
-      if (lane >= o) t += n;
-    }
+    const int t = wave_incl_scan(lane < 16 ? tmp[lane] : 0);
     if (lane < 16) tmp[16 + lane] = t - tmp[lane];  // exclusive base of each wave
   }
   __syncthreads();
