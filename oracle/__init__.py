@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+GCC_FLAGS = ["-O3", "-mavx2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
 
 
 def build(force: bool = False) -> str:

@@ -31,7 +31,7 @@
  * of code products are exact integers. The readings taken where the pages
  * leave a step open are stated beside each function.
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * Build: gcc -O3 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  * -ffp-contract=off matters: every fused multiply-add below is written as
  * fmaf() and every other product/sum must round on its own.
  */
@@ -314,51 +314,80 @@ void or_quant_mxfp4(int R, int K, const float* v, uint8_t* codes, uint8_t* scale
  * MXFP4 activations (codes cx, scales ex):
  *   isum_b = sum (2 cx_i)(2 cw_i);  acc = acc + isum_b * 2^(ex_b + ew_b - 256)
  *   out_n  = acc
- * (Each product isum_b * 2^m is exact; only the fp32 additions round.) */
+ * (Each term isum_b * 2^m is one correctly rounded operation, exact while it
+ * stays in the normal range; only the fp32 additions round.) */
 static void twice_table(int t[16])
 {
     for (int c = 0; c < 16; ++c) t[c] = twice_e2m1(c);
 }
 
-static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t* wc,
-                          const uint8_t* ws, float* out)
+/* Twice the E2M1 value of each of the K codes of a row, as small integers. */
+static void twice_row(int K, const uint8_t* codes, int8_t* out)
 {
     int t2[16];
     twice_table(t2);
-    for (int n = 0; n < N; ++n) {
-        const uint8_t* row = wc + (size_t)n * (K / 2);
-        float acc = 0.0f;
-        for (int b = 0; b < K / 32; ++b) {
-            int32_t isum = 0;
-            for (int i = 0; i < 32; ++i) {
-                int k = 32 * b + i;
-                isum += (int32_t)q[k] * t2[nibble(row, k)];
-            }
-            acc = acc + ldexpf((float)isum, (int)ws[(size_t)n * (K / 32) + b] - 128);
-        }
-        out[n] = s * acc;
+    for (int k = 0; k < K; ++k) out[k] = (int8_t)t2[nibble(codes, k)];
+}
+
+/* isum * 2^m rounded once to fp32, as ldexpf((float)isum, m) gives it
+ * (|isum| < 2^24, so (float)isum is exact). Where 2^m is itself an fp32 value
+ * the product with it is that same single rounding. */
+static float times_pow2(int32_t isum, int m)
+{
+    if (m >= -149 && m <= 127) {
+        uint32_t bits = m >= -126 ? (uint32_t)(m + 127) << 23 : 1u << (m + 149);
+        float p;
+        memcpy(&p, &bits, 4);
+        return (float)isum * p;
     }
+    return ldexpf((float)isum, m);
+}
+
+/* Rows of activations against decoded weights: xv[R][K] are the activation
+ * integers of R rows (q for int8, twice the E2M1 value for MXFP4), wd[N][K]
+ * twice the weight values. xs = NULL selects int8 (exponent e_b - 128, each
+ * row times its s[r] at the end); otherwise xs[R][K/32] are the activation
+ * E8M0 bytes (exponent ex_b + ew_b - 256). out[R][N]. Each output is the
+ * single-row formula above; the rows share the reads of a weight row. */
+static void gemm_rows_decoded(int K, int N, int R, const int8_t* xv, const uint8_t* xs, const float* s,
+                              const int8_t* wd, const uint8_t* ws, float* out)
+{
+    for (int n = 0; n < N; ++n) {
+        const int8_t* row = wd + (size_t)n * K;
+        const uint8_t* sc = ws + (size_t)n * (K / 32);
+        for (int r = 0; r < R; ++r) {
+            const int8_t* x = xv + (size_t)r * K;
+            float acc = 0.0f;
+            for (int b = 0; b < K / 32; ++b) {
+                int32_t isum = 0;
+                for (int i = 0; i < 32; ++i) isum += (int32_t)x[32 * b + i] * (int32_t)row[32 * b + i];
+                int m = xs ? (int)xs[(size_t)r * (K / 32) + b] + (int)sc[b] - 256 : (int)sc[b] - 128;
+                acc = acc + times_pow2(isum, m);
+            }
+            out[(size_t)r * N + n] = xs ? acc : s[r] * acc;
+        }
+    }
+}
+
+static void gemm_row_int8(int K, int N, const int8_t* q, float s, const uint8_t* wc,
+                          const uint8_t* ws, float* out)
+{
+    int8_t* wd = (int8_t*)malloc((size_t)N * K);
+    for (int n = 0; n < N; ++n) twice_row(K, wc + (size_t)n * (K / 2), wd + (size_t)n * K);
+    gemm_rows_decoded(K, N, 1, q, NULL, &s, wd, ws, out);
+    free(wd);
 }
 
 static void gemm_row_mxfp4(int K, int N, const uint8_t* xc, const uint8_t* xs, const uint8_t* wc,
                            const uint8_t* ws, float* out)
 {
-    int t2[16];
-    twice_table(t2);
-    for (int n = 0; n < N; ++n) {
-        const uint8_t* row = wc + (size_t)n * (K / 2);
-        float acc = 0.0f;
-        for (int b = 0; b < K / 32; ++b) {
-            int32_t isum = 0;
-            for (int i = 0; i < 32; ++i) {
-                int k = 32 * b + i;
-                isum += t2[nibble(xc, k)] * t2[nibble(row, k)];
-            }
-            int sh = (int)xs[b] + (int)ws[(size_t)n * (K / 32) + b] - 256;
-            acc = acc + ldexpf((float)isum, sh);
-        }
-        out[n] = acc;
-    }
+    int8_t* xv = (int8_t*)malloc((size_t)K);
+    int8_t* wd = (int8_t*)malloc((size_t)N * K);
+    twice_row(K, xc, xv);
+    for (int n = 0; n < N; ++n) twice_row(K, wc + (size_t)n * (K / 2), wd + (size_t)n * K);
+    gemm_rows_decoded(K, N, 1, xv, xs, NULL, wd, ws, out);
+    free(xv);
+    free(wd);
 }
 
 /* a = (g * sigmoid(g)) * u, two fp32 multiplies in that order; g = h[0:I],
@@ -428,30 +457,103 @@ static int layer_given_routing(const or_config* c, const float* xf, const int32_
     size_t as_row = mx ? (size_t)I / 32 : sizeof(float);
     float* y = (float*)malloc((size_t)P * H * sizeof(float));
 
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int p = 0; p < P; ++p) {
-        int t = p / k, e = ids[p];
-        float* h = (float*)malloc((size_t)2 * I * sizeof(float));
-        float* a = (float*)malloc((size_t)I * sizeof(float));
-        uint8_t* aq = (uint8_t*)malloc(aq_row);
-        uint8_t* asp = (uint8_t*)malloc(as_row);
-        if (mx)
-            gemm_row_mxfp4(H, 2 * I, xq + (size_t)t * xq_row, xs + (size_t)t * xs_row, w13[e], w13s[e], h);
-        else
-            gemm_row_int8(H, 2 * I, (const int8_t*)(xq + (size_t)t * xq_row),
-                          ((const float*)xs)[t], w13[e], w13s[e], h);
-        silu_mul(I, h, a);
-        if (mx) or_quant_mxfp4(1, I, a, aq, asp);
-        else or_quant_int8(1, I, a, (int8_t*)aq, (float*)asp);
-        if (mx)
-            gemm_row_mxfp4(I, H, aq, asp, w2[e], w2s[e], y + (size_t)p * H);
-        else
-            gemm_row_int8(I, H, (const int8_t*)aq, *(const float*)asp, w2[e], w2s[e], y + (size_t)p * H);
-        if (h_out) memcpy(h_out + (size_t)p * 2 * I, h, (size_t)2 * I * sizeof(float));
-        if (aq_out) memcpy((uint8_t*)aq_out + (size_t)p * aq_row, aq, aq_row);
-        if (as_out) memcpy((uint8_t*)as_out + (size_t)p * as_row, asp, as_row);
-        free(asp); free(h); free(a); free(aq);
+    /* Activation integers of x per token: q itself (int8) or twice the E2M1
+     * values of the codes (MXFP4). */
+    int8_t* xv = (int8_t*)malloc((size_t)T * H);
+    for (int t = 0; t < T; ++t) {
+        if (mx) twice_row(H, xq + (size_t)t * xq_row, xv + (size_t)t * H);
+        else memcpy(xv + (size_t)t * H, xq + (size_t)t * xq_row, (size_t)H);
     }
+
+    /* The pairs are taken expert by expert (ascending pair index within an
+     * expert) in blocks of up to PB, after each used expert's codes have been
+     * decoded to integers once; a block's rows share the reads of the decoded
+     * weights. The arithmetic of every pair is the same whatever the order. */
+    enum { PB = 8 };
+    int32_t* order = (int32_t*)malloc((size_t)P * sizeof(int32_t));
+    int32_t* start = (int32_t*)calloc((size_t)c->E + 1, sizeof(int32_t));
+    for (int p = 0; p < P; ++p) start[ids[p] + 1]++;
+    for (int e = 0; e < c->E; ++e) start[e + 1] += start[e];
+    {
+        int32_t* fill = (int32_t*)calloc((size_t)c->E, sizeof(int32_t));
+        for (int p = 0; p < P; ++p) order[start[ids[p]] + fill[ids[p]]++] = p;
+        free(fill);
+    }
+    /* decoded weights of the used experts: slot[e] = index into dec, or -1 */
+    int32_t* slot = (int32_t*)malloc((size_t)c->E * sizeof(int32_t));
+    int nused = 0;
+    for (int e = 0; e < c->E; ++e) slot[e] = start[e + 1] > start[e] ? nused++ : -1;
+    const size_t d13 = (size_t)2 * I * H, d2 = (size_t)H * I;
+    int8_t* dec = (int8_t*)malloc((size_t)nused * (d13 + d2));
+#pragma omp parallel for schedule(dynamic, 64)
+    for (long long i = 0; i < (long long)c->E * (2 * I + H); ++i) {
+        int e = (int)(i / (2 * I + H)), n = (int)(i % (2 * I + H));
+        if (slot[e] < 0) continue;
+        int8_t* base = dec + (size_t)slot[e] * (d13 + d2);
+        if (n < 2 * I) twice_row(H, w13[e] + (size_t)n * (H / 2), base + (size_t)n * H);
+        else twice_row(I, w2[e] + (size_t)(n - 2 * I) * (I / 2), base + d13 + (size_t)(n - 2 * I) * I);
+    }
+    /* task list: (expert, first index into order) per block */
+    int ntask = 0;
+    for (int e = 0; e < c->E; ++e) ntask += (start[e + 1] - start[e] + PB - 1) / PB;
+    int32_t* task = (int32_t*)malloc((size_t)(ntask + 1) * sizeof(int32_t));
+    int32_t* task_e = (int32_t*)malloc((size_t)(ntask + 1) * sizeof(int32_t));
+    ntask = 0;
+    for (int e = 0; e < c->E; ++e)
+        for (int i = start[e]; i < start[e + 1]; i += PB) {
+            task[ntask] = i;
+            task_e[ntask++] = e;
+        }
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int tk = 0; tk < ntask; ++tk) {
+        const int e = task_e[tk], i0 = task[tk];
+        const int R = (start[e + 1] - i0) < PB ? (start[e + 1] - i0) : PB;
+        const int8_t* wd13 = dec + (size_t)slot[e] * (d13 + d2);
+        const int8_t* wd2 = wd13 + d13;
+        int8_t* xr = (int8_t*)malloc((size_t)PB * H);
+        uint8_t* xsr = (uint8_t*)malloc((size_t)PB * (H / 32));
+        float sr[PB], sa[PB];
+        float* h = (float*)malloc((size_t)PB * 2 * I * sizeof(float));
+        float* a = (float*)malloc((size_t)I * sizeof(float));
+        uint8_t* aq = (uint8_t*)malloc((size_t)PB * aq_row);
+        uint8_t* asp = (uint8_t*)malloc((size_t)PB * (I / 32 + 4));
+        int8_t* av = (int8_t*)malloc((size_t)PB * I);
+        float* yb = (float*)malloc((size_t)PB * H * sizeof(float));
+        /* gather the block's activation rows */
+        for (int r = 0; r < R; ++r) {
+            int t = order[i0 + r] / k;
+            memcpy(xr + (size_t)r * H, xv + (size_t)t * H, (size_t)H);
+            if (mx) memcpy(xsr + (size_t)r * (H / 32), xs + (size_t)t * xs_row, (size_t)H / 32);
+            else sr[r] = ((const float*)xs)[t];
+        }
+        /* gate/up, SiLU-mul, requantization */
+        gemm_rows_decoded(H, 2 * I, R, xr, mx ? xsr : NULL, sr, wd13, w13s[e], h);
+        for (int r = 0; r < R; ++r) {
+            silu_mul(I, h + (size_t)r * 2 * I, a);
+            if (mx) {
+                or_quant_mxfp4(1, I, a, aq + (size_t)r * aq_row, asp + (size_t)r * (I / 32));
+                twice_row(I, aq + (size_t)r * aq_row, av + (size_t)r * I);
+            } else {
+                or_quant_int8(1, I, a, (int8_t*)aq + (size_t)r * aq_row, &sa[r]);
+                memcpy(av + (size_t)r * I, aq + (size_t)r * aq_row, (size_t)I);
+            }
+        }
+        /* down */
+        gemm_rows_decoded(I, H, R, av, mx ? asp : NULL, sa, wd2, w2s[e], yb);
+        for (int r = 0; r < R; ++r) {
+            int p = order[i0 + r];
+            memcpy(y + (size_t)p * H, yb + (size_t)r * H, (size_t)H * sizeof(float));
+            if (h_out) memcpy(h_out + (size_t)p * 2 * I, h + (size_t)r * 2 * I, (size_t)2 * I * sizeof(float));
+            if (aq_out) memcpy((uint8_t*)aq_out + (size_t)p * aq_row, aq + (size_t)r * aq_row, aq_row);
+            if (as_out) {
+                if (mx) memcpy((uint8_t*)as_out + (size_t)p * as_row, asp + (size_t)r * (I / 32), as_row);
+                else memcpy((uint8_t*)as_out + (size_t)p * as_row, &sa[r], as_row);
+            }
+        }
+        free(xr); free(xsr); free(h); free(a); free(aq); free(asp); free(av); free(yb);
+    }
+    free(task); free(task_e); free(dec); free(slot); free(order); free(start); free(xv);
 
     /* combine: acc = fma(w_j, y_j, acc) over ascending slots, from 0 */
 #pragma omp parallel for schedule(static)
