@@ -290,7 +290,7 @@ def run_ep_rank(name: str, ranks: int, steps: int, warmup: int, torch, B, S, SD,
     local = {n: lay[n].view(w.E, -1)[per * r:per * (r + 1)].contiguous() for n in ("w13", "w13s", "w2", "w2s")}
     del lay
     Pl = len(pairs)
-    lcfg = B.make_config(Pl, w.H, w.I, per, 1, w.x_dtype, w.act_mode)
+    lcfg = B.make_config(Pl, w.H, w.I, per, 1, w.x_dtype, w.act_mode, B.MOE_LAYOUT_PREPACKED)
     ws = SD.workspace(lcfg)
     out = torch.empty((Pl, w.H), dtype=torch.float32, device="cuda")
 

@@ -20,6 +20,8 @@ MOE_OK = 0
 MOE_X_F32, MOE_X_BF16 = 0, 1
 MOE_ACT_INT8, MOE_ACT_MXFP4 = 0, 1
 MOE_W13, MOE_W2 = 0, 1
+MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PREPACKED = 0, 1
+MOE_BLOCK_M_INT8, MOE_BLOCK_M_MXFP4 = 16, 64
 STAGES = ["router", "topk", "quant_x", "sort", "gate_up", "requant", "down", "combine"]
 
 # every function that include/fp4moe.h declares
@@ -40,7 +42,8 @@ class MoEError(RuntimeError):
 
 
 class moe_config(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("T", "H", "I", "E", "top_k", "x_dtype", "act_mode")]
+    _fields_ = [(n, C.c_int32) for n in ("T", "H", "I", "E", "top_k", "x_dtype", "act_mode", "block_m",
+                                         "weight_layout")]
 
     def __repr__(self):
         return "moe_config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -119,8 +122,9 @@ def status_string(status: int) -> str:
     return lib().moe_status_string(status).decode()
 
 
-def make_config(T, H, I, E, top_k, x_dtype=MOE_X_BF16, act_mode=MOE_ACT_INT8) -> moe_config:
-    return moe_config(T, H, I, E, top_k, x_dtype, act_mode)
+def make_config(T, H, I, E, top_k, x_dtype=MOE_X_BF16, act_mode=MOE_ACT_INT8, weight_layout=MOE_LAYOUT_CANONICAL,
+                block_m=0) -> moe_config:
+    return moe_config(T, H, I, E, top_k, x_dtype, act_mode, block_m, weight_layout)
 
 
 # ------------------------------------------------------------------ C ABI --

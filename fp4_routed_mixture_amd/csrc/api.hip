@@ -33,6 +33,9 @@ int check_shape(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->x_dtype != MOE_X_F32 && c->x_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
   if (c->act_mode != MOE_ACT_INT8 && c->act_mode != MOE_ACT_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout != MOE_LAYOUT_CANONICAL && c->weight_layout != MOE_LAYOUT_PREPACKED) return MOE_ERR_INVALID_ARG;
+  const int bm = c->act_mode == MOE_ACT_MXFP4 ? moe_k_prefill_block_m() : moe_k_decode_block_m();
+  if (c->block_m != 0 && c->block_m != bm) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->T < 0 || c->T > (1 << 20)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->H < 256 || c->H > 16384 || c->H % 256) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->I < 128 || c->I > 16384 || c->I % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -42,7 +45,7 @@ int check_shape(const moe_config* c) {
     // the prefill GEMMs address activation rows with 32-bit byte offsets:
     // tokens x H/2 (gate/up) and padded pair rows x I/2 (down) stay below 2^32
     const uint64_t P = (uint64_t)c->T * c->top_k;
-    const uint64_t cap = P + (uint64_t)(c->E < (int64_t)P ? c->E : P) * 63;
+    const uint64_t cap = P + (uint64_t)(c->E < (int64_t)P ? c->E : P) * (bm - 1);
     if ((uint64_t)c->T * (c->H / 2) >= (1ull << 32) || cap * (c->I / 2) >= (1ull << 32))
       return MOE_ERR_UNSUPPORTED_SHAPE;
   }
@@ -276,6 +279,9 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (overlaps(workspace, p.total, x, xbytes) || overlaps(workspace, p.total, out, (size_t)T * H * 4))
     return MOE_ERR_ALIAS;
+  // int8 taps convert the FP8 hi/lo planes with the row scales: both or none
+  if (taps && !mx && ((!taps->xq) != (!taps->xs) || (!taps->aq) != (!taps->as))) return MOE_ERR_INVALID_ARG;
+  const int canon = cfg->weight_layout == MOE_LAYOUT_CANONICAL;
 
   hipStream_t s = (hipStream_t)stream;
   float* logits = at<float>(workspace, p.logits);
@@ -344,13 +350,13 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   // expert GEMMs
   if (mx) {
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
-    MOE_TRY(moe_k_prefill_gemm(1, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, ntiles, p.max_tiles, H,
+    MOE_TRY(moe_k_prefill_gemm(1, canon, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, ntiles, p.max_tiles, H,
                                I / 32, k, P, 1, aq, (uint8_t*)as, nullptr, I, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
-    MOE_TRY(moe_k_prefill_gemm(0, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
+    MOE_TRY(moe_k_prefill_gemm(0, canon, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
                                H / 32, k, P, 0, nullptr, nullptr, y, H, s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
@@ -358,14 +364,14 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE + 1));
   } else {
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
-    MOE_TRY(moe_k_decode_gate_up(w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I, k,
+    MOE_TRY(moe_k_decode_gate_up(canon, w13, w13_scale, xq, (const float*)xs, sorted, tiles, ntiles, p.max_tiles, H, I, k,
                                  P, a, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
     MOE_TRY(moe_k_requant_rows(a, I, pos, P, aq, (float*)as, s));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
-    MOE_TRY(moe_k_decode_down(w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, H, I, k, P, y,
+    MOE_TRY(moe_k_decode_down(canon, w2, w2_scale, aq, (const float*)as, sorted, tiles, ntiles, p.max_tiles, H, I, k, P, y,
                               s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));
@@ -381,12 +387,10 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
       if (taps->aq) MOE_TRY(moe_k_gather_rows(aq, I / 2, pos, P, taps->aq, s));
       if (taps->as) MOE_TRY(moe_k_gather_rows(as, I / 32, pos, P, taps->as, s));
     } else {
-      if (taps->xq || taps->xs) {
-        if (!taps->xq || !taps->xs) return MOE_ERR_INVALID_ARG;
+      if (taps->xq) {
         MOE_TRY(moe_k_fp8pair_to_int8(xq, (const float*)xs, H, nullptr, T, (int8_t*)taps->xq, (float*)taps->xs, s));
       }
-      if (taps->aq || taps->as) {
-        if (!taps->aq || !taps->as) return MOE_ERR_INVALID_ARG;
+      if (taps->aq) {
         MOE_TRY(moe_k_fp8pair_to_int8(aq, (const float*)as, I, pos, P, (int8_t*)taps->aq, (float*)taps->as, s));
       }
     }

@@ -19,6 +19,13 @@
 // 1 KB (16 B per lane), loaded non-temporally (each weight byte is used by
 // one workgroup only).
 //
+// Weights are read in either layout: the prepacked one (each wave's load of
+// a 32x64 tile is one contiguous 1 KB) or the canonical row-major one, where
+// lane l reads 16 bytes of row l % 32 at K offset (l / 32) * 32 of each
+// K-step (32 rows x 32 bytes a load, a 128-byte line per row over a group of
+// four K-steps) and picks its four scale bytes out of the row's eight bytes
+// for the group.
+//
 // Epilogues write plain fp32 results; the steps that need whole rows or all
 // of a token's pairs run as separate small kernels after the kernel boundary:
 //   gate/up: a = (g * sigmoid(g)) * u into a[pos][I]  (then requant_rows)
@@ -53,15 +60,36 @@ __device__ __forceinline__ v4i ld_weights(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
+// The scale dword of a canonical row for K-step group g (K-steps 4g..4g+3):
+// the row's E8M0 bytes 8g..8g+7 hold blocks (step, half) = 2 step + half, so
+// lane half h takes bytes h, h+2, h+4, h+6. A last group with two K-steps
+// (K % 256 == 128) reads only its four bytes and gives the missing steps
+// scale 1 (their operands are zero).
+__device__ __forceinline__ uint32_t canon_scale_dword(const uint8_t* row_scales, int g, int KT, int h) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row_scales + 8 * g);
+  const uint32_t lo = p[0], hi = (4 * g + 2 < KT) ? p[1] : 0x7f7f7f7fu;
+  const uint32_t a = h ? (lo >> 8) : lo, b = h ? (hi >> 8) : hi;
+  return (a & 0xffu) | ((a >> 8) & 0xff00u) | ((b & 0xffu) << 16) | ((b << 8) & 0xff000000u);
+}
+
 // S = 2: a second 32-row tile, the up half of a W13 tile pair (interleaved
 // per K-step: a_step = 2048, a1 at +1024, scales at +64 dwords) or the next
 // W2 row tile (a_step = 1024, a1 at +KT*1024, scales at +G*64 dwords).
-template <int S>
+// CANON: aptr / sptr are the lane's canonical code row (+ 16 h) and scale
+// row; a_step = 32, a1_off / s1_off the distance to the second row in bytes.
+template <int S, bool CANON>
 __device__ __forceinline__ void load_group(Group<S>& G, const uint8_t* aptr, const uint32_t* sptr, const uint8_t* bptr,
                                            bool valid, int g, int KT, uint32_t a_step, uint32_t a1_off,
                                            uint32_t s_step, uint32_t s1_off) {
-  G.sa0 = sptr[(size_t)g * s_step];
-  G.sa1 = S == 2 ? sptr[(size_t)g * s_step + s1_off] : 0u;
+  if (CANON) {
+    const uint8_t* srow = reinterpret_cast<const uint8_t*>(sptr);
+    const int h = (threadIdx.x >> 5) & 1;
+    G.sa0 = canon_scale_dword(srow, g, KT, h);
+    G.sa1 = S == 2 ? canon_scale_dword(srow + s1_off, g, KT, h) : 0u;
+  } else {
+    G.sa0 = sptr[(size_t)g * s_step];
+    G.sa1 = S == 2 ? sptr[(size_t)g * s_step + s1_off] : 0u;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int kt = g * 4 + u;
@@ -99,7 +127,7 @@ __device__ __forceinline__ void mma_group(const Group<S>& G, v16f& acc0, v16f& a
 // wave's partial sums (read by the epilogue after __syncthreads()).
 // PAIRED: the two tiles are a W13 gate/up pair (tile pair j of NT pairs);
 // otherwise S tiles S*j .. S*j+S-1 of the NT row tiles of W2.
-template <int S, bool PAIRED>
+template <int S, bool PAIRED, bool CANON>
 __device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
                                                 const uint8_t* __restrict__ act8, int row, bool valid, int part, int e,
                                                 int j, int K, int NT, float (*red)[S][16][64]) {
@@ -109,16 +137,35 @@ __device__ __forceinline__ void decode_mainloop(const uint8_t* __restrict__ wq, 
   const uint8_t* bptr = act8 + ((size_t)row * 2 + part) * K + h * 16;
   const uint32_t sb = part ? 0x7f7f7f7fu : 0x83838383u;  // lo: 2^0, hi: 2^4
   constexpr int TS = PAIRED ? 2 : 1;  // 32-row tiles per NT unit
-  const size_t tile = (size_t)e * NT + (PAIRED ? j : (size_t)S * j);
-  const uint8_t* aptr = wq + tile * KT * (TS * 1024) + lane * 16;
-  const uint32_t* sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (TS * 256)) + lane;
-  const uint32_t a_step = TS * 1024, a1_off = PAIRED ? 1024u : (uint32_t)KT * 1024;
-  const uint32_t s_step = TS * 64, s1_off = PAIRED ? 64u : (uint32_t)G * 64;
+  const uint8_t* aptr;
+  const uint32_t* sptr;
+  uint32_t a_step, a1_off, s_step, s1_off;
+  if (CANON) {
+    // rows: W13 gate j*32 + c and up I + j*32 + c (N = 2I = 64 NT);
+    // W2 (2j)*32 + c and (2j+1)*32 + c (N = 32 NT)
+    const int N = PAIRED ? NT * 64 : NT * 32, c = lane & 31;
+    const int r0 = (PAIRED ? j : S * j) * 32 + c;
+    const int dr = PAIRED ? N / 2 : 32;
+    aptr = wq + ((size_t)e * N + r0) * (K >> 1) + h * 16;
+    sptr = reinterpret_cast<const uint32_t*>(wsc + ((size_t)e * N + r0) * (K >> 5));
+    a_step = 32;
+    a1_off = (uint32_t)dr * (K >> 1);
+    s_step = 0;
+    s1_off = (uint32_t)dr * (K >> 5);
+  } else {
+    const size_t tile = (size_t)e * NT + (PAIRED ? j : (size_t)S * j);
+    aptr = wq + tile * KT * (TS * 1024) + lane * 16;
+    sptr = reinterpret_cast<const uint32_t*>(wsc + tile * G * (TS * 256)) + lane;
+    a_step = TS * 1024;
+    a1_off = PAIRED ? 1024u : (uint32_t)KT * 1024;
+    s_step = TS * 64;
+    s1_off = PAIRED ? 64u : (uint32_t)G * 64;
+  }
   const int g0 = (G * wave) / NW, g1 = (G * (wave + 1)) / NW;
   v16f acc0 = {}, acc1 = {};
   for (int g = g0; g < g1; ++g) {
     Group<S> cur;
-    load_group<S>(cur, aptr, sptr, bptr, valid, g, KT, a_step, a1_off, s_step, s1_off);
+    load_group<S, CANON>(cur, aptr, sptr, bptr, valid, g, KT, a_step, a1_off, s_step, s1_off);
     mma_group<S>(cur, acc0, acc1, sb);
   }
 #pragma unroll
@@ -139,6 +186,7 @@ __device__ __forceinline__ float reduced(float (*red)[S][16][64], int s, int v, 
   return t;
 }
 
+template <bool CANON>
 __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ x8,
     const float* __restrict__ xs, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
@@ -161,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
   const bool valid = pair < P;
   const int row = valid ? pair / top_k : 0;
   const float s = xs[row];
-  decode_mainloop<2, true>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
+  decode_mainloop<2, true, CANON>(wq, wsc, x8, row, valid, part, e, j, K, NT, red);
 
   // a = (g * sigmoid(g)) * u for the hi-column lanes' rows (lane l: sort row
   // q DM + l % 16, the pair loaded above)
@@ -177,6 +225,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gate_up_kernel(
   }
 }
 
+template <bool CANON>
 __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ aq8,
     const float* __restrict__ as, const int32_t* __restrict__ sorted, const int32_t* __restrict__ tile_expert,
@@ -194,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void decode_down_kernel(
   asm volatile("" ::"s"(nt), "s"(e), "v"(pair), "v"(s));
   if (q >= nt) return;
   const bool valid = pair < P;
-  decode_mainloop<2, false>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
+  decode_mainloop<2, false, CANON>(wq, wsc, aq8, p, valid, part, e, j, K, NT, red);
 
   const int l = lane, vq = threadIdx.x >> 6;
   if ((l & 31) >= 16 || !valid) return;  // lane l: sort row p, its pair above
@@ -274,13 +323,17 @@ __global__ __launch_bounds__(256) void requant_rows_kernel(const float* __restri
 
 int moe_k_decode_block_m() { return DM; }
 
-hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
+hipError_t moe_k_decode_gate_up(int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
                                 const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
                                 int max_tiles, int H, int I, int top_k, int P, float* a, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   dim3 grid(I / 32, max_tiles);
-  decode_gate_up_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32, top_k, P,
-                                                  a, I);
+  if (canon)
+    decode_gate_up_kernel<true><<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32,
+                                                          top_k, P, a, I);
+  else
+    decode_gate_up_kernel<false><<<grid, 64 * NW, 0, st>>>(wq, wsc, x8, xs, sorted, tile_expert, n_tiles, H, I / 32,
+                                                           top_k, P, a, I);
   return hipGetLastError();
 }
 
@@ -291,12 +344,16 @@ hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* pos, int P, 
   return hipGetLastError();
 }
 
-hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
+hipError_t moe_k_decode_down(int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
                              int H, int I, int top_k, int P, float* y, hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
   dim3 grid(H / 64, max_tiles);  // two 32-row tiles per workgroup (H % 256 == 0)
-  decode_down_kernel<<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32, top_k, P, y,
-                                               H);
+  if (canon)
+    decode_down_kernel<true><<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32,
+                                                       top_k, P, y, H);
+  else
+    decode_down_kernel<false><<<grid, 64 * NW, 0, st>>>(wq, wsc, aq8, as, sorted, tile_expert, n_tiles, I, H / 32,
+                                                        top_k, P, y, H);
   return hipGetLastError();
 }

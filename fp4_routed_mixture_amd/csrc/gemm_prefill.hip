@@ -30,6 +30,12 @@
 // Launch order: blockIdx.x = weight block, so the sort tiles of one expert
 // for one weight block land on the same XCD and share its L2.
 //
+// Weights in the canonical row-major layout (CANON) take the same path with
+// another address map: lane l reads 16 bytes of its tile row l % 32 at K
+// offset 32 kt + 16 (l / 32) (32 rows x 32 bytes a load instead of one
+// contiguous 1 KB), and builds its scale dword from the row's eight E8M0
+// bytes of the group.
+//
 // Epilogue W13: a = (g * sigmoid(g)) * u, then MXFP4 requantization of each
 // 32-block along I (a 32-row gate tile is exactly one block): lanes l and
 // l^32 hold the block's two halves, one shuffle gives the block amax.
@@ -73,6 +79,14 @@ __device__ __forceinline__ uint32_t pick_scales(uint32_t vx, uint32_t vy, int h)
   return (lo & 0xffu) | ((lo >> 8) & 0xff00u) | ((hi & 0xffu) << 16) | ((hi << 8) & 0xff000000u);
 }
 
+// A canonical weight row's scale dword for group g: its E8M0 bytes 8g..8g+7,
+// of which a last group with two K-steps (K % 256 == 128) has only the first
+// four (the other two steps are never selected; they get scale 1).
+__device__ __forceinline__ uint32_t canon_row_scales(const uint8_t* row_scales, int g, int KT, int h) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(row_scales + 8 * g);
+  return pick_scales(p[0], (4 * g + 2 < KT) ? p[1] : 0x7f7f7f7fu, h);
+}
+
 // The sort tile's pair-row scales (KD dwords a row) into LDS rows of KD + 1
 // dwords: eight loads in flight per thread before their stores.
 __device__ __forceinline__ void stage_row_scales(const uint8_t* __restrict__ act_scales, const int* lds_row, int rows,
@@ -97,7 +111,7 @@ __device__ __forceinline__ void stage_row_scales(const uint8_t* __restrict__ act
   }
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool CANON>
 __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act_codes,
     const uint8_t* __restrict__ act_scales, const int32_t* __restrict__ sorted,
@@ -121,14 +135,23 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
   const int unit0 = (nb * NWAVE + wave) * UPW;
   const bool w_valid = unit0 < NT;
   const int ubase = w_valid ? unit0 : 0;  // invalid waves compute a real block and store nothing
-  const uint8_t* a_base = wq + ((size_t)e * NT + ubase) * KT * (S * 1024) + lane * 16;
+  // canonical rows: W13 tile t = gate/up half t%2 of pair ubase + t/2, row
+  // (t%2) N/2 + (ubase + t/2) 32 + c of N = 64 NT; W2 tile t: row (ubase + t) 32 + c
+  const int NR = GATE_UP ? NT * 64 : NT * 32;
+  auto canon_row = [&](int t) -> uint32_t {
+    return GATE_UP ? (uint32_t)((t & 1) * (NR >> 1) + (ubase + (t >> 1)) * 32) : (uint32_t)((ubase + t) * 32);
+  };
+  const uint8_t* a_base = CANON ? wq + ((size_t)e * NR + c) * (K >> 1) + h * 16
+                                : wq + ((size_t)e * NT + ubase) * KT * (S * 1024) + lane * 16;
   // tile t: W13 pair t/2, half t%2; W2 tile t
   auto a_ptr = [&](int t, int kt) {
-    const uint32_t off = GATE_UP ? (uint32_t)(t >> 1) * KT * 2048 + (t & 1) * 1024 + (uint32_t)kt * 2048
-                                 : (uint32_t)t * KT * 1024 + (uint32_t)kt * 1024;
+    const uint32_t off = CANON ? canon_row(t) * (uint32_t)(K >> 1) + (uint32_t)kt * 32
+                         : GATE_UP ? (uint32_t)(t >> 1) * KT * 2048 + (t & 1) * 1024 + (uint32_t)kt * 2048
+                                   : (uint32_t)t * KT * 1024 + (uint32_t)kt * 1024;
     return reinterpret_cast<const v4i*>(a_base + off);
   };
   const uint32_t* sa_base = reinterpret_cast<const uint32_t*>(wsc + ((size_t)e * NT + ubase) * G * (S * 256)) + lane;
+  const uint8_t* sa_canon = wsc + ((size_t)e * NR + c) * KB;
 
   // ---- gathered pair rows: NBL loads of 64 rows x 64 bytes per stage -------
   // load m: thread -> row 64m + tid/4, 16-byte chunk tid%4 of the stage's 64 bytes
@@ -184,9 +207,13 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
     g = g < G ? g : G - 1;
 #pragma unroll
     for (int t = 0; t < WTW; ++t) {
-      // W13: (pair * G + g) * 128 + half * 64; W2: (tile * G + g) * 64
-      const uint32_t idx = GATE_UP ? ((uint32_t)(t >> 1) * G + g) * 128 + (t & 1) * 64 : ((uint32_t)t * G + g) * 64;
-      da[t] = sa_base[idx];
+      if (CANON) {
+        da[t] = canon_row_scales(sa_canon + canon_row(t) * (uint32_t)KB, g, KT, h);
+      } else {
+        // W13: (pair * G + g) * 128 + half * 64; W2: (tile * G + g) * 64
+        const uint32_t idx = GATE_UP ? ((uint32_t)(t >> 1) * G + g) * 128 + (t & 1) * 64 : ((uint32_t)t * G + g) * 64;
+        da[t] = sa_base[idx];
+      }
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -381,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
 
 int moe_k_prefill_block_m() { return BM; }
 
-hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
+hipError_t moe_k_prefill_gemm(int gate_up, int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
                               const uint8_t* act_scales, const int32_t* sorted, const int32_t* tile_expert,
                               const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
                               int rows_are_tokens, uint8_t* aq, uint8_t* as, float* y, int out_n, hipStream_t st) {
@@ -397,18 +424,24 @@ hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc
   static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
   const hipError_t e = moe::once_per_device(lds_opt_in, [] {
     const int cap = 160 * 1024 - 4 * B_STAGE - 2 * BM * 4 - 1024;
-    hipError_t r = hipFuncSetAttribute((const void*)prefill_gemm_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, cap);
-    if (r == hipSuccess)
-      r = hipFuncSetAttribute((const void*)prefill_gemm_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, cap);
+    const void* fns[4] = {(const void*)prefill_gemm_kernel<true, false>, (const void*)prefill_gemm_kernel<false, false>,
+                          (const void*)prefill_gemm_kernel<true, true>, (const void*)prefill_gemm_kernel<false, true>};
+    hipError_t r = hipSuccess;
+    for (int i = 0; i < 4 && r == hipSuccess; ++i)
+      r = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, cap);
     return r;
   });
   if (e != hipSuccess) return e;
-  if (gate_up)
-    prefill_gemm_kernel<true><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles, K,
-                                                    NT, top_k, P, rows_are_tokens, aq, as, y, out_n);
-  else
-    prefill_gemm_kernel<false><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles,
-                                                     K, NT, top_k, P, rows_are_tokens, aq, as, y, out_n);
+#define MOE_PREFILL_LAUNCH(G1, CN)                                                                                 \
+  prefill_gemm_kernel<G1, CN><<<grid, 256, lds, st>>>(wq, wsc, act_codes, act_scales, sorted, tile_expert, n_tiles, \
+                                                      K, NT, top_k, P, rows_are_tokens, aq, as, y, out_n)
+  if (gate_up) {
+    if (canon) MOE_PREFILL_LAUNCH(true, true);
+    else MOE_PREFILL_LAUNCH(true, false);
+  } else {
+    if (canon) MOE_PREFILL_LAUNCH(false, true);
+    else MOE_PREFILL_LAUNCH(false, false);
+  }
+#undef MOE_PREFILL_LAUNCH
   return hipGetLastError();
 }

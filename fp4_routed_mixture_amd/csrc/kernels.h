@@ -52,21 +52,21 @@ hipError_t moe_k_fp8pair_to_int8(const uint8_t* src, const float* src_s, int K, 
 hipError_t moe_k_gather_rows(const void* src, int row_bytes, const int32_t* row_of, int nrows, void* dst,
                              hipStream_t st);
 
-// gemm_decode.hip
+// gemm_decode.hip (canon: weights in the canonical row-major layout instead
+// of the prepacked one)
 int moe_k_decode_block_m();
-hipError_t moe_k_decode_gate_up(const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
+hipError_t moe_k_decode_gate_up(int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* x8, const float* xs,
                                 const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles,
                                 int max_tiles, int H, int I, int top_k, int P, float* a, hipStream_t st);
 hipError_t moe_k_requant_rows(const float* a, int I, const int32_t* pos, int P, uint8_t* aq8, float* as,
                               hipStream_t st);
-hipError_t moe_k_decode_down(const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
+hipError_t moe_k_decode_down(int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* aq8, const float* as,
                              const int32_t* sorted, const int32_t* tile_expert, const int32_t* n_tiles, int max_tiles,
                              int H, int I, int top_k, int P, float* y, hipStream_t st);
 
 // gemm_prefill.hip
 int moe_k_prefill_block_m();
-int moe_k_prefill_jb();
-hipError_t moe_k_prefill_gemm(int gate_up, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
+hipError_t moe_k_prefill_gemm(int gate_up, int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
                               const uint8_t* act_scales, const int32_t* sorted, const int32_t* tile_expert,
                               const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
                               int rows_are_tokens, uint8_t* aq, uint8_t* as, float* y, int out_n, hipStream_t st);

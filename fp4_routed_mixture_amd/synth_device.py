@@ -97,8 +97,10 @@ def activations(w: S.Workload, layer: int = 0, device="cuda", T: int | None = No
     return torch.from_numpy(x).to(device)
 
 
-def config(w: S.Workload, T: int | None = None) -> B.moe_config:
-    return B.make_config(w.T if T is None else T, w.H, w.I, w.E, w.top_k, w.x_dtype, w.act_mode)
+def config(w: S.Workload, T: int | None = None, weight_layout: int = B.MOE_LAYOUT_PREPACKED) -> B.moe_config:
+    """The layer's configuration; weights as load_layer places them (prepacked)
+    unless weight_layout says otherwise."""
+    return B.make_config(w.T if T is None else T, w.H, w.I, w.E, w.top_k, w.x_dtype, w.act_mode, weight_layout)
 
 
 def workspace(cfg: B.moe_config, device="cuda") -> torch.Tensor:

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define FP4MOE_ABI_VERSION 1
+#define FP4MOE_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum moe_status {
@@ -89,19 +89,33 @@ enum moe_status {
 enum moe_x_dtype { MOE_X_F32 = 0, MOE_X_BF16 = 1 };       /* activation element type */
 enum moe_act_mode { MOE_ACT_INT8 = 0, MOE_ACT_MXFP4 = 1 }; /* activation quantization */
 enum moe_weight { MOE_W13 = 0, MOE_W2 = 1 };               /* which expert matrix */
+enum moe_weight_layout {
+    MOE_LAYOUT_CANONICAL = 0, /* the interchange layout described under "weights" below */
+    MOE_LAYOUT_PREPACKED = 1  /* the MFMA operand layout that moe_prepack writes (faster) */
+};
+
+/* Sort block sizes of the expert GEMMs: rows of one expert that one GEMM
+ * tile covers (the expert segments of the sort are padded to a multiple). */
+#define MOE_BLOCK_M_INT8 16
+#define MOE_BLOCK_M_MXFP4 64
 
 /* Layer shape and modes. act_mode selects the quantization of x and of the
  * intermediate activation (it changes the numbers, so it is never chosen
  * automatically): MOE_ACT_INT8 runs the low-M decode kernels, MOE_ACT_MXFP4
- * the scaled-FP4 MFMA grouped GEMM. */
+ * the scaled-FP4 MFMA grouped GEMM. A zero-initialized tail (block_m = 0,
+ * weight_layout = MOE_LAYOUT_CANONICAL) selects the defaults. */
 typedef struct moe_config {
-    int32_t T;        /* tokens in the batch */
-    int32_t H;        /* hidden size */
-    int32_t I;        /* expert intermediate size */
-    int32_t E;        /* routed experts */
-    int32_t top_k;    /* experts per token */
-    int32_t x_dtype;  /* enum moe_x_dtype */
-    int32_t act_mode; /* enum moe_act_mode */
+    int32_t T;             /* tokens in the batch */
+    int32_t H;             /* hidden size */
+    int32_t I;             /* expert intermediate size */
+    int32_t E;             /* routed experts */
+    int32_t top_k;         /* experts per token */
+    int32_t x_dtype;       /* enum moe_x_dtype */
+    int32_t act_mode;      /* enum moe_act_mode */
+    int32_t block_m;       /* 0 = the GEMMs' own (MOE_BLOCK_M_INT8 or MOE_BLOCK_M_MXFP4 for
+                              act_mode); any other value must equal it, else
+                              MOE_ERR_UNSUPPORTED_SHAPE */
+    int32_t weight_layout; /* enum moe_weight_layout of w13/w2 in the forward calls */
 } moe_config;
 
 /* Optional copies of intermediate results of moe_forward_taps (any pointer
@@ -153,8 +167,13 @@ const char* moe_status_string(int status);
 /* The hipError_t of this thread's last MOE_ERR_HIP (0 if none). */
 int moe_last_hip_error(void);
 
-/* Bytes of device workspace moe_forward / moe_forward_taps / moe_sort need
- * for this configuration (256-byte aligned base required). */
+/* Bytes of device workspace that moe_route, moe_router_logits, moe_sort,
+ * moe_forward, moe_forward_taps and moe_forward_routed need for this
+ * configuration (the scratch of the layer of the gfx90a paper's abstract:
+ * router partial sums, routing, the expert sort, the quantized activations
+ * and the per-pair down projections). The caller allocates it (256-byte
+ * aligned base) and may reuse it between calls on one stream.
+ * Errors: MOE_ERR_INVALID_ARG (NULL cfg or bytes, bad enum), MOE_ERR_UNSUPPORTED_SHAPE. */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* ---------------------------------------------------------------- weights --
@@ -168,16 +187,24 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *   W2  (which = MOE_W2, N = H rows, K = I): codes [E][H][I/2], scales
  *       [E][H][I/32].
  *   In a code byte the low nibble is the even element along K.
- * moe_forward reads the PREPACKED layout that moe_prepack writes: tiles of
- * 32 rows x 64 K in the operand order of the gfx950 32x32x64 scaled MFMA,
- * gate and up tiles interleaved, scales grouped four K-tiles to a dword. The
- * packing is a bijection; moe_unpack inverts it.
+ * The forward calls read either layout (cfg->weight_layout). The PREPACKED
+ * layout that moe_prepack writes is the faster one: tiles of 32 rows x 64 K in
+ * the operand order of the gfx950 32x32x64 scaled MFMA (each K-step of a tile
+ * is one contiguous 1 KiB), gate and up tiles interleaved, scales grouped four
+ * K-steps to a dword. It has the same byte count as the canonical layout (the
+ * scales pad to a multiple of four K-steps); moe_unpack inverts the packing.
  *
- * The load-time layout repair of the gfx90a paper (abstract) is
- * row_perm (device int32 [N], or NULL for the identity) makes packed row r
+ * The load-time layout repair of the gfx90a paper (abstract: the routed W2
+ * rows were stored in another order than the kernels assumed, and the fix
+ * repairs the layout when the weights are loaded) is row_perm: a device
+ * int32 [N] permutation, or NULL for the identity, that makes packed row r
  * hold canonical row row_perm[r] of every expert, codes and scales together.
  * A matrix whose rows were stored in the permuted order pi is repaired by
- * passing the inverse permutation. */
+ * passing the inverse permutation. Errors: MOE_ERR_UNSUPPORTED_SHAPE unless
+ * K % 64 == 0 and N % 64 == 0 (W13) or N % 32 == 0 (W2); MOE_ERR_ALIGNMENT
+ * for code pointers not 16-byte aligned; MOE_ERR_ALIAS when the packed and
+ * canonical buffers overlap. row_perm must be a permutation of 0..N-1 (not
+ * checked: an entry outside it reads outside the expert's rows). */
 int moe_prepacked_size(int32_t which, int32_t E, int32_t N, int32_t K,
                        size_t* code_bytes, size_t* scale_bytes);
 int moe_prepack(int32_t which, int32_t E, int32_t N, int32_t K,
@@ -188,16 +215,26 @@ int moe_unpack(int32_t which, int32_t E, int32_t N, int32_t K,
                uint8_t* codes, uint8_t* scales, void* stream);
 
 /* ---------------------------------------------------------------- router --
- * Sigmoid-score top-k routing. x: [T][H] fp32 or bf16 (cfg->x_dtype),
- * router_w: fp32 [E][H], router_bias: fp32 [E] or NULL (added to the logit
- * before the sigmoid, so it moves selection and weights).
- * Outputs: topk_ids int32 [T][top_k] in selection order (highest score
- * first), topk_w fp32 [T][top_k] renormalized weights:
- * S = ((s_0 + s_1) + s_2) + ..., w_j = s_j / S (1/top_k if S == 0). */
+ * Sigmoid-score top-k routing: each token picks top_k of the E routed experts
+ * (DeepSeek V4 Flash on 8x AMD gfx1201, What we set out to do: 256 routed
+ * experts, 6 active per token; the per-token expert selection whose hashes
+ * the gfx90a paper checks, abstract).
+ *   x          [T][H] fp32 or bf16 (cfg->x_dtype), row-major, 16-byte aligned
+ *   router_w   fp32 [E][H], 16-byte aligned
+ *   router_bias fp32 [E] or NULL: added to the logit before the sigmoid, so
+ *              it moves selection and weights
+ *   topk_ids   int32 [T][top_k] out: experts in selection order (highest
+ *              score first; equal scores: lower expert first)
+ *   topk_w     fp32 [T][top_k] out: S = ((s_0 + s_1) + s_2) + ..., w_j = s_j / S
+ *              (1/top_k if S == 0)
+ *   workspace  at least moe_workspace_size(cfg) bytes, 256-byte aligned
+ * Errors: MOE_ERR_INVALID_ARG (NULL pointer, bad enum), MOE_ERR_UNSUPPORTED_SHAPE,
+ * MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. */
 int moe_route(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
               int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The router logits alone, as moe_route computes them before the sigmoid:
+/* The router logits alone (the scores of the routing of the gfx90a paper,
+ * abstract, before the sigmoid), as moe_route computes them:
  * logits fp32 [T][E] (device, caller-owned, overwritten),
  * l[t][e] = pdot(x[t], router_w[e]) + router_bias[e], where pdot splits H
  * into 64 contiguous chunks, sums each chunk as a chain of fused
@@ -218,7 +255,12 @@ int moe_router_logits(const moe_config* cfg, const void* x, const float* router_
  *   pair_pos [P]        padded position of each pair
  *   tile_expert [cap / block_m + 1]  expert of each block_m tile, in order
  *   n_tiles [1]         offsets[E] / block_m  (stays on the device)
- * Bit-exact: integers only. */
+ * Bit-exact: integers only. Only cfg->T, cfg->top_k and cfg->E are read.
+ * All arrays are device memory owned by the caller; workspace as for
+ * moe_workspace_size (its sort scratch). Errors: MOE_ERR_INVALID_ARG (NULL
+ * pointer), MOE_ERR_UNSUPPORTED_SHAPE (block_m out of range),
+ * MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. ids outside
+ * [0, E) are not allowed (not checked). */
 int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids,
              int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
              int32_t* tile_expert, int32_t* n_tiles,
@@ -229,27 +271,44 @@ int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids,
  * MOE_X_BF16) with cfg->act_mode (int8 rows as the gfx90a paper quantizes
  * decode activations, abstract; MXFP4 per OCP Microscaling v1.0).
  *   INT8 : q int8 [rows][K], scales fp32 [rows]. K % 64 == 0.
- *   MXFP4: q codes [rows][K/2], scales E8M0 [rows][K/32]. K % 64 == 0. */
+ *   MXFP4: q codes [rows][K/2], scales E8M0 [rows][K/32]. K % 64 == 0.
+ * Only cfg->act_mode is read. v, q: 16-byte aligned device memory owned by
+ * the caller; scales: device memory. Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED_SHAPE (K outside 64..65536 or not a multiple of 64),
+ * MOE_ERR_ALIGNMENT, MOE_ERR_HIP. */
 int moe_quantize(const moe_config* cfg, int32_t rows, int32_t K, int32_t in_dtype,
                  const void* v, void* q, void* scales, void* stream);
 
 /* --------------------------------------------------------------- forward --
- * The whole routed-MoE layer: route, sort, quantize x, gate/up GEMM with
- * fused SiLU*mul and requantization, down GEMM, weighted combine.
+ * The whole routed-MoE layer with FP4 packed expert weights and int8 or MXFP4
+ * activations (the routed experts of the gfx90a paper, abstract: FP4 experts,
+ * int8 decode activations, the expert sort, MFMA prefill): route, sort,
+ * quantize x, gate/up GEMM with fused SiLU*mul and requantization, down
+ * GEMM, weighted combine.
  *   x [T][H] (cfg->x_dtype), router_w fp32 [E][H], router_bias fp32 [E] or
- *   NULL, w13/w13_scale and w2/w2_scale in the prepacked layout,
+ *   NULL, w13/w13_scale and w2/w2_scale in the layout cfg->weight_layout
+ *   names (canonical or prepacked, see "weights"; all 16-byte aligned),
  *   out fp32 [T][H] (overwritten; must not overlap x),
  *   topk_ids_out int32 [T][top_k] and topk_w_out fp32 [T][top_k] or NULL,
- *   workspace of at least moe_workspace_size(cfg) bytes, 256-byte aligned. */
+ *   workspace of at least moe_workspace_size(cfg) bytes, 256-byte aligned.
+ * Every pointer is device memory owned by the caller; nothing is kept.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE (shape limits, or a
+ * block_m other than the GEMMs'), MOE_ERR_ALIGNMENT, MOE_ERR_ALIAS (out over
+ * x, or the workspace over x or out), MOE_ERR_WORKSPACE_TOO_SMALL,
+ * MOE_ERR_HIP; nothing is launched on an error other than MOE_ERR_HIP. */
 int moe_forward(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                 const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
                 float* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_forward that also copies the intermediates named in taps and records
- * the stage events (NULL taps = moe_forward). The copies are extra kernels
- * after the layer. sorted_pairs needs P + min(E, P) * (block_m - 1) entries
- * (block_m = 16 for MOE_ACT_INT8, 128 for MOE_ACT_MXFP4). */
+ * the stage events (NULL taps = moe_forward), for the fixed-token and hash
+ * checks of the gfx90a paper (abstract). The copies are extra kernels after
+ * the layer. sorted_pairs needs P + min(E, P) * (block_m - 1) entries with
+ * block_m = MOE_BLOCK_M_INT8 (16) for MOE_ACT_INT8 and MOE_BLOCK_M_MXFP4 (64)
+ * for MOE_ACT_MXFP4 (the value written to taps->block_m). xq and xs, and aq
+ * and as, come in pairs: one without the other is MOE_ERR_INVALID_ARG,
+ * reported before anything is launched. */
 int moe_forward_taps(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
                      const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
                      float* out, int32_t* topk_ids_out, float* topk_w_out, const moe_taps* taps,
@@ -290,7 +349,7 @@ int moe_residual_add(int64_t n, float* x, const float* y, void* stream);
  * with x fp32 [T][H] updated in place (cfg->x_dtype must be MOE_X_F32; the
  * layer's input is the normalized stream, fp32). Per-layer device pointers
  * come in HOST arrays of length L: router_w[l], w13[l], w13_scale[l], w2[l],
- * w2_scale[l] (prepacked), router_bias[l] (router_bias itself or any entry
+ * w2_scale[l] (layout cfg->weight_layout), router_bias[l] (router_bias itself or any entry
  * may be NULL). layer_out (device fp32 [L][T][H], nullable) receives every
  * layer's moe output, for teacher-forced checks of one layer at a time.
  * workspace: at least moe_stack_workspace_size bytes, 256-byte aligned, not

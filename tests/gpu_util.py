@@ -3,6 +3,8 @@ binding, oracle inputs from the host generators (never from the device)."""
 from __future__ import annotations
 
 import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -32,9 +34,12 @@ def host_x(w: S.Workload, layer=0, T=None) -> np.ndarray:
 
 def oracle_experts(w: S.Workload, ids: np.ndarray, layer: int = 0):
     """Per-expert canonical weights from the host generator for the experts
-    that appear in ids (None elsewhere)."""
-    need = set(np.unique(ids).tolist())
-    return [S.expert_weights(w, layer, e) if e in need else None for e in range(w.E)]
+    that appear in ids (None elsewhere); generated on a thread pool (numpy
+    releases the GIL in its integer loops)."""
+    need = sorted(set(np.unique(ids).tolist()))
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        got = dict(zip(need, ex.map(lambda e: S.expert_weights(w, layer, e), need)))
+    return [got.get(e) for e in range(w.E)]
 
 
 def oracle_layer(w: S.Workload, x_rows: np.ndarray, layer: int = 0, intermediates=False, wr=None, bias="default"):

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.moe_abi_version() == 1
+    assert B.moe_abi_version() == 2
     for s in range(7):
         assert B.moe_status_string(s) and B.moe_status_string(s) != "unknown status"
     assert B.moe_status_string(99) == "unknown status"
@@ -42,9 +42,42 @@ def test_version_and_status_strings(L):
 
 
 def cfg(**kw):
-    base = dict(T=4, H=4096, I=2048, E=256, top_k=6, x_dtype=1, act_mode=0)
+    base = dict(T=4, H=4096, I=2048, E=256, top_k=6, x_dtype=1, act_mode=0, block_m=0, weight_layout=1)
     base.update(kw)
-    return B.moe_config(*(base[n] for n in ("T", "H", "I", "E", "top_k", "x_dtype", "act_mode")))
+    return B.moe_config(*(base[n] for n in ("T", "H", "I", "E", "top_k", "x_dtype", "act_mode", "block_m",
+                                            "weight_layout")))
+
+
+def header_define(name):
+    m = re.search(r"#define\s+" + name + r"\s+(\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_config_struct_matches_header(L):
+    """The binding's moe_config has the header's fields in the header's order."""
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct moe_config \{(.*?)\} moe_config;", src, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert [n for n, _ in B.moe_config._fields_] == fields
+    assert C.sizeof(B.moe_config) == 4 * len(fields)
+    assert (B.MOE_BLOCK_M_INT8, B.MOE_BLOCK_M_MXFP4) == (header_define("MOE_BLOCK_M_INT8"),
+                                                         header_define("MOE_BLOCK_M_MXFP4"))
+
+
+def test_block_m_and_weight_layout_fields(L):
+    """block_m: 0 or the GEMMs' own block size for the activation mode;
+    weight_layout: canonical (0) or prepacked (1)."""
+    for mode, bm in ((0, header_define("MOE_BLOCK_M_INT8")), (1, header_define("MOE_BLOCK_M_MXFP4"))):
+        assert ws_status(cfg(act_mode=mode, block_m=0))[0] == 0
+        assert ws_status(cfg(act_mode=mode, block_m=bm))[0] == 0
+        assert ws_status(cfg(act_mode=mode, block_m=bm * 2))[0] == 2
+        assert ws_status(cfg(act_mode=mode, block_m=-1))[0] == 2
+    assert ws_status(cfg(weight_layout=0))[0] == 0
+    assert ws_status(cfg(weight_layout=2))[0] == 1
+    assert ws_status(cfg(weight_layout=-1))[0] == 1
+    # a zero-initialized tail is the default: canonical weights, the GEMMs' block size
+    c = B.make_config(4, 4096, 2048, 256, 6)
+    assert c.block_m == 0 and c.weight_layout == B.MOE_LAYOUT_CANONICAL
 
 
 def ws_status(c):
@@ -105,6 +138,17 @@ def test_forward_argument_errors(L):
     assert fwd(c, ws_bytes=100) == 5
     assert fwd(cfg(H=100)) == 2
     assert fwd(cfg(T=0), x=None, out=None) == 0  # empty batch: nothing to do
+
+
+def test_forward_taps_pairs_checked_before_launch(L):
+    """int8 taps of x (or of the activation) need both the codes and the
+    scales: one alone is refused before anything is launched."""
+    c = cfg()
+    for named in (("xq",), ("xs",), ("aq",), ("as_",)):
+        t = B.moe_taps(**{n: FAKE + (1 << 36) for n in named})
+        st = L.moe_forward_taps(C.byref(c), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 30), None, None,
+                                C.byref(t), FAKE + (1 << 34), 1 << 40, None)
+        assert st == 1, named
 
 
 def test_routed_forward_errors(L):

@@ -1,6 +1,7 @@
 """GPU parity of the whole layer (moe_forward through the C ABI) against the
-oracle, at small sizes element by element and at the full workload sizes on
-sampled tokens (every output depends only on its own token)."""
+oracle: element by element at small sizes, on every token of the 4,604-token
+prefill batch, and on one token of every sort tile of the 16,384-token chunk
+(every output depends only on its own token)."""
 import numpy as np
 import pytest
 import torch
@@ -69,25 +70,62 @@ def test_forward_decode_full(name):
     print(f"max|err| {err:.3g} rms {rms:.3g}")
 
 
-def _sample_tokens(w, ids, n, seed=0):
-    """Tokens that include the heaviest expert's, the lightest experts', the
-    last token (ragged tail) and random ones."""
-    rng = np.random.default_rng(seed)
-    T = ids.shape[0]
-    load = np.bincount(ids.ravel(), minlength=w.E)
-    heavy = np.argmax(load)
-    light = [e for e in np.argsort(load) if load[e] > 0][:3]
-    pick = {0, T - 1, int(np.nonzero((ids == heavy).any(1))[0][-1])}
-    for e in light:
-        pick.add(int(np.nonzero((ids == e).any(1))[0][0]))
-    while len(pick) < n:
-        pick.add(int(rng.integers(0, T)))
-    return np.array(sorted(pick))
+def _compare_prefill(g, o, toks, w):
+    """Rows toks of a GPU prefill call against the oracle's layer on those
+    tokens: quantized x and requantized activations byte for byte, y and out
+    within 2e-3 x RMS (MXFP4 down sums need more than fp32's 24 bits, so
+    they round in another order)."""
+    assert np.array_equal(g["xq"][toks], o["xq"])
+    assert np.array_equal(g["xs"][toks], o["xs"])
+    pairs = (toks[:, None] * w.top_k + np.arange(w.top_k)).ravel()
+    flips = int((g["aq"][pairs] != o["aq"]).sum())
+    print(f"requant byte differences: {flips} of {o['aq'].size}")
+    assert flips == 0
+    assert np.array_equal(g["as"][pairs], o["as"])
+    assert_close_rms(g["y"][pairs], o["y"], what="y")
+    err, rms = assert_close_rms(g["out"][toks], o["out"])
+    print(f"{len(toks)} tokens, {len(pairs)} pairs: max|err| {err:.3g} rms {rms:.3g}")
 
 
-@pytest.mark.parametrize("name,n", [("prefill_t4604_zipf", 48), ("prefill_t16384_zipf", 24),
-                                    ("prefill_t4604_zipf_tp4", 32)])
-def test_forward_prefill_sampled(name, n):
+@pytest.mark.parametrize("name", ["prefill_t4604_zipf", "prefill_t4604_zipf_tp4"])
+def test_forward_prefill_full(name):
+    """Every token of the 4,604-token prefill batch (and its tensor-parallel
+    shard) against the oracle's whole layer."""
+    w = S.WORKLOADS[name]
+    print(f"[forward] {S.describe(w)}", flush=True)
+    g = run_forward(w, dev_layer(name), SD.activations(w), taps=True)
+    o = oracle_layer(w, S.activations(w), intermediates=True)
+    assert np.array_equal(g["ids"], o["ids"])
+    assert np.array_equal(g["w"].view(np.uint32), o["w"].view(np.uint32))
+    _compare_prefill(g, o, np.arange(w.T), w)
+    assert np.isfinite(g["out"]).all()
+
+
+def tile_covering_tokens(ids, top_k, E, block_m, extra=()):
+    """One token from every block_m-row sort tile, at a row that moves with
+    the tile index (so every row position of a tile is exercised somewhere),
+    plus the last pair of every expert (the ragged end of its last tile) and
+    any extra tokens."""
+    s = oracle.sort(ids, E, block_m)
+    srt, P = s["sorted"], ids.size
+    pick = set(int(t) for t in extra)
+    for q in range(s["n_tiles"]):
+        rows = srt[q * block_m:(q + 1) * block_m]
+        valid = rows[rows < P]
+        pick.add(int(valid[(37 * q) % len(valid)]) // top_k)
+    for e in range(E):
+        seg = srt[s["offsets"][e]:s["offsets"][e + 1]]
+        seg = seg[seg < P]
+        if len(seg):
+            pick.add(int(seg[-1]) // top_k)
+    return np.array(sorted(pick)), s["n_tiles"]
+
+
+def test_forward_prefill_16k_tiles():
+    """The 16,384-token chunk, in the call the benchmark times: routing bit
+    for bit over all tokens, and the layer on one token of every sort tile
+    (about 1,700 tiles), every expert's ragged last tile and the batch ends."""
+    name = "prefill_t16384_zipf"
     w = S.WORKLOADS[name]
     print(f"[forward] {S.describe(w)}", flush=True)
     g = run_forward(w, dev_layer(name), SD.activations(w), taps=True)
@@ -95,16 +133,11 @@ def test_forward_prefill_sampled(name, n):
     ids_o, w_o = oracle.route(x_h, S.router_weights(w), S.router_bias(w), w.top_k)
     assert np.array_equal(g["ids"], ids_o)
     assert np.array_equal(g["w"].view(np.uint32), w_o.view(np.uint32))
-    toks = _sample_tokens(w, ids_o, n)
+    toks, n_tiles = tile_covering_tokens(ids_o, w.top_k, w.E, g["block_m"], extra=(0, w.T - 1))
+    print(f"{n_tiles} sort tiles of {g['block_m']} rows -> {len(toks)} tokens", flush=True)
+    assert len(toks) >= n_tiles // w.top_k
     o = oracle_layer(w, x_h[toks], intermediates=True)
-    assert np.array_equal(g["xq"][toks], o["xq"])
-    pairs = (toks[:, None] * w.top_k + np.arange(w.top_k)).ravel()
-    flips = int((g["aq"][pairs] != o["aq"]).sum())
-    print(f"requant byte differences: {flips} of {o['aq'].size}")
-    assert flips == 0
-    err, rms = assert_close_rms(g["out"][toks], o["out"])
-    print(f"max|err| {err:.3g} rms {rms:.3g}")
-    # full-output properties that hold at any size
+    _compare_prefill(g, o, toks, w)
     assert np.isfinite(g["out"]).all()
 
 

@@ -26,7 +26,7 @@ def _gpu():
 
 def _routed(w, lay, x, ids, wts, E=None, taps=None):
     T, k = ids.shape
-    cfg = B.make_config(T, w.H, w.I, w.E if E is None else E, k, w.x_dtype, w.act_mode)
+    cfg = B.make_config(T, w.H, w.I, w.E if E is None else E, k, w.x_dtype, w.act_mode, B.MOE_LAYOUT_PREPACKED)
     ws = SD.workspace(cfg)
     out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
     B.moe_forward_routed(cfg, x, ids, wts, lay["w13"], lay["w13s"], lay["w2"], lay["w2s"], out, ws, taps=taps)

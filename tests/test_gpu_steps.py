@@ -115,20 +115,30 @@ LOGIT_CASES = [(4, 4096, 256, S.X_BF16), (16, 4096, 256, S.X_F32), (17, 4096, 25
 
 
 @pytest.mark.parametrize("T,H,E,xd", LOGIT_CASES)
-@pytest.mark.parametrize("data", ["normal", "wide"])
+@pytest.mark.parametrize("data", ["normal", "wide", "subnormal"])
 def test_router_logits_bitexact(T, H, E, xd, data):
     """moe_router_logits equals the oracle's pinned reduction order bit for bit.
     'wide' scales every operand by 2^-12 .. 2^12, so the products of one
     logit span 48 binades and nearly every partial sum rounds: a reduction
-    that differed from chained fmas in ascending k anywhere would show."""
+    that differed from chained fmas in ascending k anywhere would show.
+    'subnormal' puts nearly all products below 2^-126 (subnormal fp32) and
+    most chunk sums too, with logits on both sides of 2^-126: a step that
+    flushed subnormal inputs or results to zero would show."""
     rng = np.random.default_rng(T * 7 + H + E)
     if data == "normal":
         x32 = rng.standard_normal((T, H)).astype(np.float32)
         wr = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    elif data == "subnormal":
+        x32 = (rng.standard_normal((T, H)) * np.exp2(rng.integers(-6, 7, (T, H)) - 62.0)).astype(np.float32)
+        wr = (rng.standard_normal((E, H)) * np.exp2(rng.integers(-6, 7, (E, H)) - 74.0)).astype(np.float32)
     else:
         x32 = (rng.standard_normal((T, H)) * np.exp2(rng.integers(-12, 13, (T, H)))).astype(np.float32)
         wr = (rng.standard_normal((E, H)) * np.exp2(rng.integers(-12, 13, (E, H)) - 24.0)).astype(np.float32)
     bias = (0.5 * rng.standard_normal(E)).astype(np.float32)
+    if data == "subnormal":
+        bias = (rng.standard_normal(E) * 2.0 ** -130).astype(np.float32)  # subnormal too
+        prod = x32[0][:, None] * wr.T
+        assert ((np.abs(prod) < 2.0 ** -126) & (prod != 0)).mean() > 0.5, "the case must make subnormal products"
     if xd == S.X_F32:
         x_h, x_d = x32, torch.from_numpy(x32).cuda()
     else:
