@@ -1,18 +1,22 @@
 #!/usr/bin/env python
 """Benchmark of the FP4 routed-MoE layer on one MI355X.
 
-A step is one moe_forward (route, sort, quantize, gate/up GEMM with SiLU*mul,
-down GEMM, combine) over one batch. The headline workload is the decode layer
-with 4 tokens (hidden 4096, intermediate 2048, 256 experts, top-6, bf16 x,
-int8 activations). Steps cycle through ROT distinct layers (weights and
-inputs drawn from different seeds' streams) so each step streams expert
-weights that the previous steps did not touch, as a 43-layer model's decode
-does; the 256 MB last-level cache cannot serve them.
+The headline workload is the largest one that fits one GPU: 43 stacked MoE
+layers with distinct weights (hidden 4096, intermediate 2048, 256 experts,
+top-6, 147 GB resident), decode batch 32 with the residual stream
+x <- x + moe_l(rmsnorm(x)), int8 activations. A step is one pass of that
+batch through all 43 layers (route, sort, quantize, gate/up GEMM with
+SiLU*mul, requantization, down GEMM, combine + residual + RMSNorm per layer).
+The same workload's 16,384-token prefill chunk through one layer (MXFP4
+activations, Zipf(1.1) expert load) gives the prefill FP4 roofline object;
+the single-layer decode and prefill workloads are legs.
 
-Prints one JSON line: tokens/s, the dominant kernel's roofline fraction
-(algorithmic bytes or FLOPs per launch / its average duration from HIP events
-recorded on the library's stream inside the timed region), and the CPU
-oracle's tokens/s on a bounded sample of the same workload.
+Prints one JSON line: tokens/s with the median and 10th/90th percentile of
+the step times, the dominant kernel's roofline fraction (algorithmic bytes or
+FLOPs per launch / its average duration from HIP events recorded on the
+library's stream inside the timed region), the prefill gate/up kernel's FP4
+fraction, a streaming-read ceiling, and the CPU oracle's tokens/s on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -97,6 +101,31 @@ def graph_time(fn, reps: int, torch, sleep_ms: float = 20.0) -> float:
     return t0.elapsed_time(t1) / reps
 
 
+def step_stats(durations_ms):
+    """Median, 10th and 90th percentile of per-step durations (ms)."""
+    d = np.asarray(durations_ms, dtype=np.float64)
+    return {"median": round(float(np.median(d)), 5), "p10": round(float(np.percentile(d, 10)), 5),
+            "p90": round(float(np.percentile(d, 90)), 5), "n": int(d.size)}
+
+
+def timed_steps(step, steps, torch, sleep_ms):
+    """Run step(i) for i < steps back to back behind a bounded GPU sleep (so
+    the host's enqueueing stays ahead of the GPU), with torch events on the
+    current stream (the one the library launches on) at every step boundary.
+    Returns (total ms, per-step ms list, host enqueue seconds)."""
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda._sleep(int(sleep_ms * 2.4e6))
+    h0 = time.perf_counter()
+    bounds[0].record()
+    for i in range(steps):
+        step(i)
+        bounds[i + 1].record()
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    per = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)]
+    return bounds[0].elapsed_time(bounds[steps]), per, host_s
+
+
 def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, ev: HipEvents,
                  sleep_ms: float = 20.0, sample_every: int = 4) -> dict:
     w = S.WORKLOADS[name]
@@ -126,12 +155,9 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: a bounded GPU sleep first keeps the device busy while the
-    # host enqueues all `steps` layer calls, so the steps then run back to
-    # back and the measured time is the GPU's, not the host's launch rate.
-    # Every `sample_every`-th step records HIP events on the library's stream
-    # around its gate/up kernel (the dominant kernel); an event record costs
-    # GPU time, so sampling keeps that cost out of most steps.
+    # Timed region. Every `sample_every`-th step records HIP events on the
+    # library's stream around its gate/up kernel (the dominant kernel); an
+    # event record costs GPU time, so sampling keeps that cost out of most steps.
     g_events = []
     for i in range(steps):
         arr = (C.c_void_p * (2 * nst))()
@@ -139,16 +165,7 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
             pair = ev.create(2)
             arr[2 * gu], arr[2 * gu + 1] = pair[0], pair[1]
         g_events.append(arr)
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_ms * 2.4e6))
-    t_start.record()
-    h0 = time.perf_counter()
-    for i in range(steps):
-        step(i, g_events[i])
-    host_s = time.perf_counter() - h0
-    t_end.record()
-    torch.cuda.synchronize()
-    elapsed = t_start.elapsed_time(t_end) / 1e3
+    total_ms, per_step, host_s = timed_steps(lambda i: step(i, g_events[i]), steps, torch, sleep_ms)
     sampled = [i for i in range(steps) if i % sample_every == 0]
     g1_all = [ev.elapsed_ms(g_events[i][2 * gu], g_events[i][2 * gu + 1]) for i in sampled]
     g1_ms = float(np.mean(g1_all))
@@ -181,37 +198,42 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
         distinct.append(len(np.unique(a)))
         max_load.append(int(np.bincount(a.ravel(), minlength=w.E).max()))
     d_avg = float(np.mean([distinct[i % rot] for i in range(steps)]))
+    d_sampled = float(np.mean([distinct[i % rot] for i in sampled]))
     b13, b2 = per_expert_bytes(w)
     xbytes = T * w.H * (2 if w.x_dtype == S.X_BF16 else 4)
     P = T * w.top_k
     layer_bytes = d_avg * (b13 + b2) + w.E * w.H * 4 + xbytes + T * w.H * 4
     # gate/up kernel: weights of the routed experts + quantized x in + its output
     if w.act_mode == S.ACT_INT8:
-        g1_bytes = d_avg * b13 + T * 2 * w.H + P * w.I * 4
+        g1_bytes = d_sampled * b13 + T * 2 * w.H + P * w.I * 4
     else:
-        g1_bytes = d_avg * b13 + T * w.H // 2 + T * w.H // 32 + P * (w.I // 2 + w.I // 32)
+        g1_bytes = d_sampled * b13 + T * w.H // 2 + T * w.H // 32 + P * (w.I // 2 + w.I // 32)
     g1_flops = 2.0 * P * w.H * 2 * w.I
     layer_flops = 2.0 * P * (w.H * 2 * w.I + w.I * w.H)
-    ms_step = elapsed * 1e3 / steps
+    ms_step = total_ms / steps
     return {
         "workload": name, "T": T, "steps": steps, "rot": rot, "host_enqueue_ms": host_s * 1e3,
         "gpu_bound": host_s < sleep_ms / 1e3, "gate_up_ms_min": float(np.min(g1_all)),
-        "gate_up_samples": len(g1_all),
+        "gate_up_samples": len(g1_all), "step_ms": step_stats(per_step),
         "ms_per_step": ms_step, "tokens_per_s": T / (ms_step / 1e3),
         "graph_ms_per_step": graph_ms, "graph_tokens_per_s": T / (graph_ms / 1e3),
         "stage_ms": stage_ms, "distinct_experts": d_avg, "max_load": max_load,
         "layer_alg_bytes": layer_bytes, "layer_hbm_gbs": layer_bytes / (ms_step / 1e3) / 1e9,
         "layer_fp4_tflops": layer_flops / (ms_step / 1e3) / 1e12,
-        "gate_up_alg_bytes": g1_bytes, "gate_up_ms": g1_ms,
+        "gate_up_alg_bytes": g1_bytes, "gate_up_alg_flops": g1_flops, "gate_up_ms": g1_ms,
         "gate_up_gbs": g1_bytes / (g1_ms / 1e3) / 1e9,
         "gate_up_tflops": g1_flops / (g1_ms / 1e3) / 1e12,
     }
 
 
-def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: float = 20.0) -> dict:
+def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, ev: HipEvents, sleep_ms: float = 20.0,
+              sample_stride: int = 4) -> dict:
     """The layer stack (x <- x + moe_l(rmsnorm(x)) over all layers, distinct
-    weights per layer, all resident) through moe_forward_stack. A step is one
-    pass over every layer for one decode batch."""
+    weights per layer, all resident) through moe_forward_stack_taps. A step
+    is one pass over every layer for one decode batch, starting from the same
+    input stream (a 512 KB device copy at the step's start). In step i the
+    layers l with l % sample_stride == i % sample_stride record HIP events on
+    the library's stream around their gate/up kernel."""
     w = S.WORKLOADS[name]
     L, T = w.layers, w.T
     layers = [SD.load_layer(w, layer=l) for l in range(L)]
@@ -219,49 +241,71 @@ def run_stack(name: str, steps: int, warmup: int, torch, B, S, SD, sleep_ms: flo
     ws = torch.empty(B.moe_stack_workspace_size(cfg), dtype=torch.uint8, device="cuda")
     x0 = torch.from_numpy(S.activations(w)).cuda()
     x = x0.clone()
+    nst = len(B.STAGES)
+    gu = B.STAGES.index("gate_up")
     for _ in range(warmup):
+        x.copy_(x0)
         B.moe_forward_stack(cfg, x, layers, ws)
     torch.cuda.synchronize()
-    x.copy_(x0)
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_ms * 2.4e6))
-    t_start.record()
-    h0 = time.perf_counter()
-    for _ in range(steps):
-        B.moe_forward_stack(cfg, x, layers, ws)
-    host_s = time.perf_counter() - h0
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / steps
-    # the same step (all layers) replayed from one HIP graph
-    graph_ms = graph_time(lambda: B.moe_forward_stack(cfg, x, layers, ws), steps, torch, sleep_ms)
 
-    # routing of every layer on the first step's stream (diagnostic, untimed):
-    # the distinct experts each layer reads set the algorithmic bytes
+    taps, sampled = [], []
+    for i in range(steps):
+        t = [None] * L
+        for l in range(i % sample_stride, L, sample_stride):
+            arr = (C.c_void_p * (2 * nst))()
+            pair = ev.create(2)
+            arr[2 * gu], arr[2 * gu + 1] = pair[0], pair[1]
+            t[l] = {"events": arr}
+            sampled.append((i, l, arr))
+        taps.append(t)
+
+    def step(i):
+        x.copy_(x0)
+        B.moe_forward_stack_taps(cfg, x, layers, ws, taps[i])
+    total_ms, per_step, host_s = timed_steps(step, steps, torch, sleep_ms)
+    ms_step = total_ms / steps
+    g1 = [(l, ev.elapsed_ms(arr[2 * gu], arr[2 * gu + 1])) for _, l, arr in sampled]
+    for _, _, arr in sampled:
+        ev.destroy([arr[2 * gu], arr[2 * gu + 1]])
+
+    # the same step replayed from one HIP graph
+    def gstep():
+        x.copy_(x0)
+        B.moe_forward_stack(cfg, x, layers, ws)
+    graph_ms = graph_time(gstep, steps, torch, sleep_ms)
+
+    # routing of every layer of the step (diagnostic, untimed): the distinct
+    # experts each layer reads set the algorithmic bytes
     x.copy_(x0)
     y = torch.empty((L, T, w.H), dtype=torch.float32, device="cuda")
     B.moe_forward_stack(cfg, x, layers, ws, layer_out=y)
     xl = x0.clone()
-    rcfg = SD.config(w)
-    rws = SD.workspace(rcfg)
+    rws = SD.workspace(cfg)
     xn = torch.empty_like(xl)
     ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
     distinct = []
     for l in range(L):
         B.moe_rmsnorm(T, w.H, xl, xn)
-        B.moe_route(rcfg, xn, layers[l]["router_w"], layers[l]["bias"], ids, wts, rws)
+        B.moe_route(cfg, xn, layers[l]["router_w"], layers[l]["bias"], ids, wts, rws)
         distinct.append(len(np.unique(ids.cpu().numpy())))
         xl += y[l]
     b13, b2 = per_expert_bytes(w)
+    P = T * w.top_k
     step_bytes = sum(d * (b13 + b2) + w.E * w.H * 4 + 2 * T * w.H * 4 for d in distinct)
+    # gate/up launches: the layer's routed experts' W13 + int8 x as FP8 hi/lo planes + fp32 activation out
+    g1_bytes = [distinct[l] * b13 + T * 2 * w.H + P * w.I * 4 for l, _ in g1]
+    g1_ms = [d for _, d in g1]
     del layers
     return {"workload": name, "layers": L, "T": T, "steps": steps, "ms_per_step": ms_step,
-            "tokens_per_s": T / (ms_step / 1e3), "host_enqueue_ms": host_s * 1e3 / steps,
+            "step_ms": step_stats(per_step), "tokens_per_s": T / (ms_step / 1e3), "host_enqueue_ms": host_s * 1e3,
             "graph_ms_per_step": graph_ms, "graph_tokens_per_s": T / (graph_ms / 1e3),
-            "gpu_bound": host_s < sleep_ms / 1e3 + steps * ms_step / 1e3,
+            "gpu_bound": host_s * 1e3 < sleep_ms + total_ms,
             "distinct_experts_per_layer": float(np.mean(distinct)), "step_alg_bytes": step_bytes,
-            "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9, "graph_hbm_gbs": step_bytes / (graph_ms / 1e3) / 1e9}
+            "hbm_gbs": step_bytes / (ms_step / 1e3) / 1e9, "graph_hbm_gbs": step_bytes / (graph_ms / 1e3) / 1e9,
+            "gate_up_launches": len(g1), "gate_up_ms": float(np.mean(g1_ms)),
+            "gate_up_alg_bytes": float(np.mean(g1_bytes)),
+            "gate_up_gbs": float(np.sum(g1_bytes)) / (float(np.sum(g1_ms)) / 1e3) / 1e9}
 
 
 def run_ep_rank(name: str, ranks: int, steps: int, warmup: int, torch, B, S, SD, sleep_ms: float = 20.0) -> dict:
@@ -318,11 +362,35 @@ def run_ep_rank(name: str, ranks: int, steps: int, warmup: int, torch, B, S, SD,
 
 
 def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
-    """The oracle, untuned, on the host cores: whole layers of the same
-    workload (rotating the same seeded batches) until about budget_s of CPU
-    work; for large batches a token sample (every output depends only on its
-    own token)."""
+    """The oracle, untuned, on the host cores, on a bounded sample of the
+    same workload: for the layer stack, consecutive layers of the stack on
+    the same 32-token stream (rmsnorm, the layer, the residual add, each
+    layer's expert weights generated outside the timed region) scaled to
+    whole-stack steps; for a single layer, whole-layer calls on (at most 64 of)
+    its tokens (every output depends only on its own token)."""
     w = S.WORKLOADS[name]
+    if w.layers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        x = S.activations(w)
+        t_layers, l = 0.0, 0
+        while l < w.layers and (l == 0 or t_layers < budget_s):
+            wr, b = S.router_weights(w, l), S.router_bias(w, l)
+            ids, _ = oracle.route(oracle.rmsnorm(x), wr, b, w.top_k)  # only to know which experts to generate
+            need = sorted(set(np.unique(ids).tolist()))
+            with ThreadPoolExecutor(16) as ex:
+                got = dict(zip(need, ex.map(lambda e: S.expert_weights(w, l, e), need)))
+            ex_w = [got.get(e) for e in range(w.E)]
+            t0 = time.perf_counter()
+            xn = oracle.rmsnorm(x)
+            y = oracle.moe_layer(xn, wr, b, ex_w, w.top_k, w.act_mode)["out"]
+            x = (x + y).astype(np.float32)
+            t_layers += time.perf_counter() - t0
+            l += 1
+        per_step = t_layers / l * w.layers
+        return {"value": w.T / per_step, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"layers 0..{l - 1} of the {w.layers}-layer stack on its {w.T}-token stream "
+                          f"(rmsnorm + layer + residual), {t_layers:.1f} s of oracle work, scaled to "
+                          f"{w.layers}-layer steps; expert weight generation outside the timed region"}
     T = min(w.T, 64)
     batches = []
     for l in range(4):
@@ -348,9 +416,10 @@ def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
                       f"{el:.1f} s wall, weight generation outside the timed region"}
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the
-    kernel source is unchanged since they were taken."""
+def profiled(kernel: str, workload: str):
+    """The committed rocprofv3 counter record of a kernel on a workload (HBM
+    bytes per launch, MFMA utilisation), if the kernel's source is unchanged
+    since the counters were taken."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     try:
@@ -361,20 +430,55 @@ def traffic_for(kernel: str, workload: str):
     src = os.path.join(ROOT, "fp4_routed_mixture_amd", "csrc", rec["source"])
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
         return None
-    return rec["bytes_per_launch"]
+    return rec
+
+
+def streaming_read_gbs(torch, SD, gib: int = 8, reps: int = 5) -> float:
+    """A plain streaming read of a large buffer (nontemporal 16-byte loads,
+    8 workgroups of 256 threads per CU): the practical HBM read ceiling
+    beside the 8 TB/s peak."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    blocks = 256 * 8
+    sink = torch.empty(blocks * 16, dtype=torch.uint8, device="cuda")
+    SD.stream_read(buf, blocks, sink)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        SD.stream_read(buf, blocks, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del buf, sink
+    return (gib << 30) / (ms / 1e3) / 1e9
+
+
+def leg_summary(v: dict) -> dict:
+    return {"tokens_per_s": round(v["tokens_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
+            "step_ms": v["step_ms"],
+            "graph_tokens_per_s": round(v["graph_tokens_per_s"], 1),
+            "graph_ms_per_step": round(v["graph_ms_per_step"], 5),
+            "layer_hbm_gbs": round(v["layer_hbm_gbs"], 1),
+            "layer_hbm_frac": round(v["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "layer_fp4_tflops": round(v["layer_fp4_tflops"], 1),
+            "layer_fp4_frac": round(v["layer_fp4_tflops"] / FP4_PEAK_TFLOPS, 4),
+            "gate_up_gbs": round(v["gate_up_gbs"], 1), "gate_up_tflops": round(v["gate_up_tflops"], 1),
+            "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
+            "distinct_experts": v["distinct_experts"]}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_t4")
-    ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through")
-    ap.add_argument("--no-legs", action="store_true", help="skip the prefill and Zipf-decode legs")
-    ap.add_argument("--legs", default="decode_t64_zipf,prefill_t4604_zipf,prefill_t16384_zipf,stack43_decode_t32,"
+    ap.add_argument("--workload", default="stack43_decode_t32",
+                    help="headline workload: the 43-layer decode stack (default) or a single-layer workload")
+    ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through (single-layer workloads)")
+    ap.add_argument("--legs", default="prefill_t16384_zipf,decode_t4,decode_t64_zipf,prefill_t4604_zipf,"
                                       "decode_t4_tp4,prefill_t4604_zipf_tp4,prefill_t4604_zipf_ep8",
-                    help="comma-separated legs to run after the headline workload")
+                    help="comma-separated legs to run after the headline workload ('' for none)")
+    ap.add_argument("--no-legs", action="store_true", help="run the headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
@@ -401,104 +505,119 @@ def main():
     from fp4_routed_mixture_amd import synth_device as SD
     B.lib()
     ev = HipEvents()
+    w = S.WORKLOADS[args.workload]
+    stack_head = w.layers > 1
 
-    main_res = run_workload(args.workload, args.steps, args.warmup, args.rot, torch, B, S, SD, ev)
-    print(f"# {args.workload}: {main_res['ms_per_step'] * 1e3:.1f} us/step, {main_res['tokens_per_s']:.0f} tok/s "
-          f"(graph {main_res['graph_ms_per_step'] * 1e3:.1f} us/step), stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in main_res["stage_ms"].items()),
-          file=sys.stderr, flush=True)
+    if stack_head:
+        head = run_stack(args.workload, args.steps, args.warmup, torch, B, S, SD, ev)
+        print(f"# {args.workload}: {head['ms_per_step']:.3f} ms/step ({w.layers} layers), "
+              f"{head['tokens_per_s']:.0f} tok/s, {head['hbm_gbs']:.0f} GB/s; graph {head['graph_ms_per_step']:.3f} "
+              f"ms/step; gate/up {head['gate_up_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    else:
+        head = run_workload(args.workload, args.steps, args.warmup, args.rot, torch, B, S, SD, ev)
+        print(f"# {args.workload}: {head['ms_per_step'] * 1e3:.1f} us/step, {head['tokens_per_s']:.0f} tok/s",
+              file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
     legs = {}
-    want = set() if args.no_legs else set(args.legs.split(","))
-    stack = None
-    if want:
-        for name, steps, rot in (("decode_t64_zipf", 32, 8), ("prefill_t4604_zipf", 10, 2),
-                                 ("prefill_t16384_zipf", 4, 2), ("decode_t4_tp4", 64, 8),
-                                 ("prefill_t4604_zipf_tp4", 10, 2)):
-            if name not in want:
-                continue
-            torch.cuda.empty_cache()
-            r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev)
-            legs[name] = r
-            print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step (graph {r['graph_ms_per_step'] * 1e3:.1f}), "
-                  f"{r['tokens_per_s']:.0f} tok/s, layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; stages(us) "
-                  + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()), file=sys.stderr, flush=True)
+    want = set() if args.no_legs else set(x for x in args.legs.split(",") if x)
+    for name, steps, rot in (("prefill_t16384_zipf", 8, 2), ("decode_t4", 64, 8), ("decode_t64_zipf", 32, 8),
+                             ("prefill_t4604_zipf", 10, 2), ("decode_t4_tp4", 64, 8),
+                             ("prefill_t4604_zipf_tp4", 10, 2)):
+        if name not in want or name == args.workload:
+            continue
+        torch.cuda.empty_cache()
+        r = run_workload(name, steps, 3, rot, torch, B, S, SD, ev, sample_every=1 if "prefill" in name else 4)
+        legs[name] = r
+        print(f"# {name}: {r['ms_per_step'] * 1e3:.1f} us/step (graph {r['graph_ms_per_step'] * 1e3:.1f}), "
+              f"{r['tokens_per_s']:.0f} tok/s, layer {r['layer_hbm_gbs']:.0f} GB/s, {r['layer_fp4_tflops']:.0f} TF/s; "
+              f"stages(us) " + " ".join(f"{k}={v * 1e3:.1f}" for k, v in r["stage_ms"].items()),
+              file=sys.stderr, flush=True)
     ep = None
     if "prefill_t4604_zipf_ep8" in want:
         torch.cuda.empty_cache()
         ep = run_ep_rank("prefill_t4604_zipf", 8, 10, 2, torch, B, S, SD)
         print(f"# prefill_t4604_zipf_ep8: {ep['ms_per_step'] * 1e3:.1f} us/step, {ep['pairs']} pairs "
-              f"({100 * ep['pair_share']:.1f}% of all), {ep['fp4_tflops']:.0f} TF/s, {ep['hbm_gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
-    if "stack43_decode_t32" in want:
-        torch.cuda.empty_cache()
-        stack = run_stack("stack43_decode_t32", 5, 1, torch, B, S, SD)
-        print(f"# stack43_decode_t32: {stack['ms_per_step']:.2f} ms/step (43 layers), {stack['tokens_per_s']:.0f} "
-              f"tok/s, {stack['hbm_gbs']:.0f} GB/s; graph {stack['graph_ms_per_step']:.2f} ms/step, "
-              f"{stack['graph_tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+              f"({100 * ep['pair_share']:.1f}% of all), {ep['fp4_tflops']:.0f} TF/s", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    stream_gbs = streaming_read_gbs(torch, SD)
 
-    w = S.WORKLOADS[args.workload]
-    mx = w.act_mode == S.ACT_MXFP4
-    if mx:
-        ach, peak, unit, bound = main_res["gate_up_tflops"], FP4_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    # roofline of the dominant kernel of the headline workload
+    if stack_head:
+        kernel = "decode_gate_up_kernel"
+        prof = profiled(kernel, args.workload)
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(head["gate_up_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["gate_up_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": prof["bytes_per_launch"] if prof else None,
+                "alg_bytes_per_launch": round(head["gate_up_alg_bytes"]), "launches_timed": head["gate_up_launches"],
+                "avg_launch_us": round(head["gate_up_ms"] * 1e3, 2),
+                "step_hbm_gbs": round(head["hbm_gbs"], 1), "step_hbm_frac": round(head["hbm_gbs"] / HBM_PEAK_GBS, 4),
+                "streaming_read_gbs": round(stream_gbs, 1)}
     else:
-        ach, peak, unit, bound = main_res["gate_up_gbs"], HBM_PEAK_GBS, "GB/s", "hbm"
-    kernel = "prefill_gemm_kernel<true>" if mx else "decode_gate_up_kernel"
-    roof = {"bound": bound, "kernel": kernel, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 4), "traffic": traffic_for(kernel, args.workload),
-            "layer_hbm_gbs": round(main_res["layer_hbm_gbs"], 1),
-            "layer_hbm_frac": round(main_res["layer_hbm_gbs"] / HBM_PEAK_GBS, 4)}
+        mx = w.act_mode == S.ACT_MXFP4
+        kernel = "prefill_gemm_kernel<true>" if mx else "decode_gate_up_kernel"
+        prof = profiled(kernel, args.workload)
+        ach, peak, unit, bound = ((head["gate_up_tflops"], FP4_PEAK_TFLOPS, "TFLOP/s", "mfma") if mx else
+                                  (head["gate_up_gbs"], HBM_PEAK_GBS, "GB/s", "hbm"))
+        roof = {"bound": bound, "kernel": kernel, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": prof["bytes_per_launch"] if prof else None,
+                "avg_launch_us": round(head["gate_up_ms"] * 1e3, 2),
+                "layer_hbm_frac": round(head["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
+                "streaming_read_gbs": round(stream_gbs, 1)}
+    # the prefill chunk's FP4 roofline (the metric's "prefill FP4 MFMA % of peak")
+    roof_pf = None
+    pf = legs.get("prefill_t16384_zipf") or (head if args.workload == "prefill_t16384_zipf" else None)
+    if pf is not None:
+        k = "prefill_gemm_kernel<true>"
+        prof = profiled(k, "prefill_t16384_zipf")
+        roof_pf = {"bound": "mfma", "kernel": k, "workload": "prefill_t16384_zipf",
+                   "achieved": round(pf["gate_up_tflops"], 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(pf["gate_up_tflops"] / FP4_PEAK_TFLOPS, 4),
+                   "traffic": prof["bytes_per_launch"] if prof else None,
+                   "mfma_util_profiled": prof.get("mfma_util") if prof else None,
+                   "alg_flops_per_launch": pf["gate_up_alg_flops"], "avg_launch_us": round(pf["gate_up_ms"] * 1e3, 2),
+                   "launches_timed": pf["gate_up_samples"],
+                   "layer_fp4_tflops": round(pf["layer_fp4_tflops"], 1),
+                   "layer_fp4_frac": round(pf["layer_fp4_tflops"] / FP4_PEAK_TFLOPS, 4),
+                   "layer_tokens_per_s": round(pf["tokens_per_s"], 1)}
 
     import oracle
     cpu = cpu_baseline(args.workload, args.cpu_seconds, S, oracle)
 
     line = {
         "metric": "routed-MoE tokens/s; decode HBM GB/s and prefill FP4 MFMA % of peak",
-        "value": round(main_res["tokens_per_s"], 1),
+        "value": round(head["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": main_res["steps"],
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "step_ms": head["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4" if mx else "fp4xint8",
+        "dtype": "mxfp4" if w.act_mode == S.ACT_MXFP4 else "fp4xint8",
         "data": "synthetic",
-        "config": {"workload": args.workload, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.top_k,
-                   "x": "bf16" if w.x_dtype == S.X_BF16 else "fp32", "act": "mxfp4" if mx else "int8",
-                   "routing": "zipf1.1" if w.zipf else "uniform", "distinct_layers_cycled": args.rot},
+        "config": {"workload": args.workload, "layers": w.layers, "T": w.T, "H": w.H, "I": w.I, "E": w.E,
+                   "top_k": w.top_k, "x": "bf16" if w.x_dtype == S.X_BF16 else "fp32",
+                   "act": "mxfp4" if w.act_mode == S.ACT_MXFP4 else "int8",
+                   "routing": "zipf1.1" if w.zipf else "uniform"},
         "roofline": roof,
+        "roofline_prefill": roof_pf,
         "cpu_baseline": cpu,
-        "graph": {"ms_per_step": round(main_res["graph_ms_per_step"], 5),
-                  "tokens_per_s": round(main_res["graph_tokens_per_s"], 1)},
-        "stage_us_diagnostic": {k: round(v * 1e3, 2) for k, v in main_res["stage_ms"].items()},
-        "distinct_experts": main_res["distinct_experts"],
-        "legs": {k: {"tokens_per_s": round(v["tokens_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
-                     "graph_tokens_per_s": round(v["graph_tokens_per_s"], 1),
-                     "graph_ms_per_step": round(v["graph_ms_per_step"], 5),
-                     "layer_hbm_gbs": round(v["layer_hbm_gbs"], 1),
-                     "layer_hbm_frac": round(v["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
-                     "layer_fp4_tflops": round(v["layer_fp4_tflops"], 1),
-                     "layer_fp4_frac": round(v["layer_fp4_tflops"] / FP4_PEAK_TFLOPS, 4),
-                     "gate_up_gbs": round(v["gate_up_gbs"], 1), "gate_up_tflops": round(v["gate_up_tflops"], 1),
-                     "stage_us": {s: round(x * 1e3, 2) for s, x in v["stage_ms"].items()},
-                     "distinct_experts": v["distinct_experts"]} for k, v in legs.items()},
+        "graph": {"ms_per_step": round(head["graph_ms_per_step"], 5),
+                  "tokens_per_s": round(head["graph_tokens_per_s"], 1)},
+        "legs": {k: leg_summary(v) for k, v in legs.items()},
     }
+    if not stack_head:
+        line["stage_us_diagnostic"] = {k: round(v * 1e3, 2) for k, v in head["stage_ms"].items()}
+    else:
+        line["distinct_experts_per_layer"] = head["distinct_experts_per_layer"]
     if ep is not None:
         line["legs"]["prefill_t4604_zipf_ep8"] = {
             "workload": ep["workload"], "pairs": ep["pairs"], "pair_share": round(ep["pair_share"], 4),
             "experts_used": ep["experts_used"], "ms_per_step": round(ep["ms_per_step"], 5),
             "pairs_per_s": round(ep["pairs_per_s"], 1), "fp4_tflops": round(ep["fp4_tflops"], 1),
             "fp4_frac": round(ep["fp4_tflops"] / FP4_PEAK_TFLOPS, 4), "hbm_gbs": round(ep["hbm_gbs"], 1)}
-    if stack is not None:
-        line["legs"]["stack43_decode_t32"] = {
-            "tokens_per_s": round(stack["tokens_per_s"], 1), "ms_per_step": round(stack["ms_per_step"], 4),
-            "layers": stack["layers"], "hbm_gbs": round(stack["hbm_gbs"], 1),
-            "hbm_frac": round(stack["hbm_gbs"] / HBM_PEAK_GBS, 4),
-            "graph_tokens_per_s": round(stack["graph_tokens_per_s"], 1),
-            "graph_ms_per_step": round(stack["graph_ms_per_step"], 4),
-            "graph_hbm_frac": round(stack["graph_hbm_gbs"] / HBM_PEAK_GBS, 4),
-            "distinct_experts_per_layer": stack["distinct_experts_per_layer"],
-            "host_enqueue_ms_per_step": round(stack["host_enqueue_ms"], 3)}
     print(json.dumps(line))
 
 

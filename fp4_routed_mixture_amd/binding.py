@@ -29,7 +29,7 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_wo
            "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_router_logits", "moe_sort",
            "moe_quantize",
            "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
-           "moe_stack_workspace_size", "moe_forward_stack"]
+           "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps"]
 
 
 class MoEError(RuntimeError):
@@ -90,6 +90,7 @@ def lib():
             "moe_residual_add": (C.c_int, [i64, vp, vp, vp]),
             "moe_stack_workspace_size": (C.c_int, [cfgp, C.POINTER(sz)]),
             "moe_forward_stack": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_forward_stack_taps": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -251,3 +252,24 @@ def moe_forward_stack(cfg, x, layers, workspace, layer_out=None, stream=None):
     keep = [arr(k) for k in ("router_w", "bias", "w13", "w13s", "w2", "w2s")]
     _check(lib().moe_forward_stack(C.byref(cfg), L, _p(x), *[C.cast(a, C.c_void_p) for a in keep], _p(layer_out),
                                    _p(workspace), workspace.numel(), _s(stream)), "moe_forward_stack")
+
+
+def moe_forward_stack_taps(cfg, x, layers, workspace, layer_taps, layer_out=None, stream=None):
+    """moe_forward_stack with per-layer taps: layer_taps is a sequence of L
+    dicts (or None) as for moe_forward_taps; returns the block size used."""
+    L = len(layers)
+    arr = lambda key: (C.c_void_p * max(L, 1))(*[_p(d[key]) for d in layers])
+    keep = [arr(k) for k in ("router_w", "bias", "w13", "w13s", "w2", "w2s")]
+    bm = C.c_int32(0)
+    tps = (moe_taps * max(L, 1))()
+    for l, t in enumerate(layer_taps):
+        if t is None:
+            continue
+        ev = t.get("events")
+        tps[l] = moe_taps(*(_p(t.get(n)) for n in ("xq", "xs", "aq", "as", "y", "counts", "offsets",
+                                                   "sorted_pairs", "pair_pos")),
+                          C.cast(C.pointer(bm), C.c_void_p), None if ev is None else C.cast(ev, C.c_void_p))
+    _check(lib().moe_forward_stack_taps(C.byref(cfg), L, _p(x), *[C.cast(a, C.c_void_p) for a in keep],
+                                        _p(layer_out), C.cast(tps, C.c_void_p), _p(workspace), workspace.numel(),
+                                        _s(stream)), "moe_forward_stack_taps")
+    return bm.value

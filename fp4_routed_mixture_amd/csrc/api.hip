@@ -434,6 +434,14 @@ int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* c
                       const float* const* router_bias, const uint8_t* const* w13, const uint8_t* const* w13_scale,
                       const uint8_t* const* w2, const uint8_t* const* w2_scale, float* layer_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
+  return moe_forward_stack_taps(cfg, L, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, layer_out, nullptr,
+                                workspace, workspace_bytes, stream);
+}
+int moe_forward_stack_taps(const moe_config* cfg, int32_t L, float* x, const float* const* router_w,
+                           const float* const* router_bias, const uint8_t* const* w13,
+                           const uint8_t* const* w13_scale, const uint8_t* const* w2, const uint8_t* const* w2_scale,
+                           float* layer_out, const moe_taps* taps, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   int st = check_shape(cfg);
   if (st) return st;
   if (cfg->x_dtype != MOE_X_F32) return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -447,8 +455,12 @@ int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* c
   if (overlaps(workspace, need, x, nb) || (layer_out && overlaps(workspace, need, layer_out, nb * L)) ||
       (layer_out && overlaps(x, nb, layer_out, nb * L)))
     return MOE_ERR_ALIAS;
-  for (int l = 0; l < L; ++l)
+  for (int l = 0; l < L; ++l) {
     if (!router_w[l] || !w13[l] || !w13_scale[l] || !w2[l] || !w2_scale[l]) return MOE_ERR_INVALID_ARG;
+    if (taps && cfg->act_mode == MOE_ACT_INT8 &&
+        ((!taps[l].xq) != (!taps[l].xs) || (!taps[l].aq) != (!taps[l].as)))
+      return MOE_ERR_INVALID_ARG;
+  }
   hipStream_t s = (hipStream_t)stream;
   float* xn = at<float>(workspace, fw);
   float* ybuf = at<float>(workspace, fw + up256(nb));
@@ -461,7 +473,7 @@ int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* c
   for (int l = 0; l < L; ++l) {
     float* yl = layer_out ? layer_out + (size_t)l * cfg->T * cfg->H : ybuf;
     st = forward_impl(cfg, xn, router_w[l], router_bias ? router_bias[l] : nullptr, w13[l], w13_scale[l], w2[l],
-                      w2_scale[l], yl, nullptr, nullptr, nullptr, workspace, fw, stream, false);
+                      w2_scale[l], yl, nullptr, nullptr, taps ? &taps[l] : nullptr, workspace, fw, stream, false);
     if (st) return st;
     MOE_TRY(moe_k_combine_residual_norm(ypair, wts, cfg->T, cfg->H, cfg->top_k, x, layer_out ? yl : nullptr,
                                         l + 1 < L ? xn : nullptr, s));

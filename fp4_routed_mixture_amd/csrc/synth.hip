@@ -4,6 +4,8 @@
 // stream with key K is mix(K + (i + 1) * 0x9E3779B97F4A7C15), each output
 // gives eight little-endian bytes; a scale byte is 121 + (byte mod 5).
 // Used to place the 43-layer stack (about 147 GB) in HBM without a host copy.
+// The same benchmark-support library holds a plain streaming-read probe, the
+// practical HBM read ceiling that the weight-streaming kernels are set beside.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,9 +30,44 @@ __global__ void fill_kernel(uint64_t key, uint64_t first_word, uint64_t nwords, 
   }
 }
 
+// Every thread reads 16-byte words nontemporally in a grid-stride loop and
+// folds them with xor; one word per workgroup is written so that the loads
+// are kept. nwords16 = bytes / 16.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, uint64_t nwords16,
+                                                          u32x4* __restrict__ sink) {
+  u32x4 acc = {0, 0, 0, 0};
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < nwords16; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u];
+  }
+  for (; i < nwords16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+  __shared__ u32x4 red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32x4 t = {0, 0, 0, 0};
+    for (int k = 0; k < 256; ++k) t ^= red[k];
+    sink[blockIdx.x] = t;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Streaming read of nbytes (multiple of 16, 16-byte aligned) at src with
+// `blocks` workgroups of 256 threads; sink receives `blocks` 16-byte words.
+int synth_stream_read(const void* src, uint64_t nbytes, int blocks, void* sink, void* stream) {
+  if (!src || !sink || (nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)sink & 15) || blocks < 1) return 1;
+  stream_read_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const u32x4*)src, nbytes / 16, (u32x4*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 uint64_t synth_stream_key(int seed, int layer, int tensor) {
   uint64_t z = ((uint64_t)seed << 40) | ((uint64_t)layer << 16) | (uint64_t)tensor;

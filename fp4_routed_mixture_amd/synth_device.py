@@ -32,6 +32,8 @@ def slib():
         L.synth_fill.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
         L.synth_stream_key.restype = C.c_uint64
         L.synth_stream_key.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.synth_stream_read.restype = C.c_int
+        L.synth_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
         _slib = L
     return _slib
 
@@ -106,3 +108,12 @@ def config(w: S.Workload, T: int | None = None, weight_layout: int = B.MOE_LAYOU
 def workspace(cfg: B.moe_config, device="cuda") -> torch.Tensor:
     n = B.moe_workspace_size(cfg)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor) -> None:
+    """Enqueue the streaming-read probe over buf (a benchmark ceiling, not
+    part of the layer); sink holds blocks 16-byte words."""
+    rc = slib().synth_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), blocks, sink.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read failed ({rc})")

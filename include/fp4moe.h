@@ -361,6 +361,20 @@ int moe_forward_stack(const moe_config* cfg, int32_t L, float* x, const float* c
                       const uint8_t* const* w2, const uint8_t* const* w2_scale, float* layer_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward_stack with per-layer taps: taps is NULL or a HOST array of L
+ * moe_taps, and layer l's intermediates and stage events are handled as
+ * moe_forward_taps handles them (the combine stage is fused into the
+ * residual update and records its events around nothing; y, xq/xs, aq/as,
+ * the sort arrays and block_m are those of layer l). Used to time one stage
+ * of chosen layers on the stream the kernels run on. Same errors as
+ * moe_forward_stack, plus MOE_ERR_INVALID_ARG for an unpaired int8 tap of
+ * any layer (checked before anything is launched). */
+int moe_forward_stack_taps(const moe_config* cfg, int32_t L, float* x, const float* const* router_w,
+                           const float* const* router_bias, const uint8_t* const* w13,
+                           const uint8_t* const* w13_scale, const uint8_t* const* w2, const uint8_t* const* w2_scale,
+                           float* layer_out, const moe_taps* taps, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,3 +65,47 @@ def test_stack_teacher_forced(name, L, check):
         xn = oracle.rmsnorm(xs[l])
         o = oracle_layer(w, xn, layer=l)
         assert np.array_equal(o["out"], y[l]), f"layer {l}: max |diff| {np.abs(o['out'] - y[l]).max()}"
+
+
+def test_stack_taps_equal_stack():
+    """moe_forward_stack_taps with per-layer taps (gate/up events on some
+    layers, a layer's y and sort arrays on another) leaves the stream exactly
+    as moe_forward_stack does, and its taps hold that layer's data."""
+    w = S.Workload("stack_taps", 8, 256, 128, 8, 2, S.X_F32, S.ACT_INT8, False, 13, 4)
+    L = w.layers
+    layers = [SD.load_layer(w, l) for l in range(L)]
+    cfg = SD.config(w)
+    ws = torch.empty(B.moe_stack_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    x0 = torch.from_numpy(S.activations(w)).cuda()
+    x_ref = x0.clone()
+    y_ref = torch.empty((L, w.T, w.H), dtype=torch.float32, device="cuda")
+    B.moe_forward_stack(cfg, x_ref, layers, ws, layer_out=y_ref)
+    import ctypes as C
+    import bench
+    he = bench.HipEvents()
+    nst = len(B.STAGES)
+    gu = B.STAGES.index("gate_up")
+    evs = []
+    taps = [None] * L
+    for l in (0, 2):
+        arr = (C.c_void_p * (2 * nst))()
+        pair = he.create(2)
+        arr[2 * gu], arr[2 * gu + 1] = pair[0], pair[1]
+        evs.append(arr)
+        taps[l] = {"events": arr}
+    P = w.T * w.top_k
+    y1 = torch.empty((P, w.H), dtype=torch.float32, device="cuda")
+    pos1 = torch.empty(P, dtype=torch.int32, device="cuda")
+    taps[1] = {"y": y1, "pair_pos": pos1}
+    x = x0.clone()
+    bm = B.moe_forward_stack_taps(cfg, x, layers, ws, taps)
+    torch.cuda.synchronize()
+    assert bm == B.MOE_BLOCK_M_INT8
+    assert np.array_equal(x.cpu().numpy(), x_ref.cpu().numpy())
+    for arr in evs:
+        assert he.elapsed_ms(arr[2 * gu], arr[2 * gu + 1]) > 0
+        he.destroy([arr[2 * gu], arr[2 * gu + 1]])
+    # layer 1's y tap equals the oracle's per-pair down projections for that
+    # layer's input (int8: every step exact)
+    o = oracle_layer(w, oracle.rmsnorm((x0 + y_ref[0]).cpu().numpy()), layer=1, intermediates=True)
+    assert np.array_equal(y1.cpu().numpy(), o["y"])
