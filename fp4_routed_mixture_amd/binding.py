@@ -29,7 +29,8 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_wo
            "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_router_logits", "moe_sort",
            "moe_quantize",
            "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
-           "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps"]
+           "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps", "moe_forward_noalloc"]
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoEError(RuntimeError):
@@ -91,6 +92,7 @@ def lib():
             "moe_stack_workspace_size": (C.c_int, [cfgp, C.POINTER(sz)]),
             "moe_forward_stack": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_forward_stack_taps": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_forward_noalloc": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -193,6 +195,15 @@ def moe_forward(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out
     _check(lib().moe_forward(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(w13), _p(w13_scale), _p(w2),
                              _p(w2_scale), _p(out), _p(topk_ids_out), _p(topk_w_out), _p(workspace),
                              workspace.numel(), _s(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
+                        stream=None):
+    """moe_forward without a workspace: the library's fixed per-device
+    scratch array (MOE_NOALLOC_SCRATCH_BYTES) is used instead."""
+    _check(lib().moe_forward_noalloc(C.byref(cfg), _p(x), _p(router_w), _p(router_bias), _p(w13), _p(w13_scale),
+                                     _p(w2), _p(w2_scale), _p(out), _p(topk_ids_out), _p(topk_w_out), _s(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_forward_taps(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,

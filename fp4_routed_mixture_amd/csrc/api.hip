@@ -2,8 +2,16 @@
 // Everything here runs on the host; every computation runs in the kernels.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fp4moe.h"
 #include "kernels.h"
+
+// Scratch of moe_forward_noalloc: one fixed array per device, allocated with
+// the code object when the library is loaded on that device and held until
+// the process ends. Host code never uses this name as an address; it uses
+// the per-device address from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -421,6 +429,44 @@ int moe_forward_routed(const moe_config* cfg, const void* x, const int32_t* topk
   if (cfg && cfg->T > 0 && (!topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
   return forward_impl(cfg, x, nullptr, nullptr, w13, w13_scale, w2, w2_scale, out, nullptr, nullptr, taps, workspace,
                       workspace_bytes, stream, true, topk_ids, topk_w);
+}
+
+namespace {
+constexpr int kNoallocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoallocMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (each device holds its own copy).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kNoallocMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                        const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                        float* out, int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  int st = check_shape(cfg);
+  if (st) return st;
+  if (make_plan(cfg).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (cfg->T == 0) return MOE_OK;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  return forward_impl(cfg, x, router_w, router_bias, w13, w13_scale, w2, w2_scale, out, topk_ids_out, topk_w_out,
+                      nullptr, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 int moe_stack_workspace_size(const moe_config* cfg, size_t* bytes) {

@@ -301,6 +301,25 @@ int moe_forward(const moe_config* cfg, const void* x, const float* router_w, con
                 float* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same layer, with the scratch taken from a fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * (from the first call on that device until the process ends) instead of a
+ * caller workspace. Nothing is allocated or freed in the call. The caller
+ * still passes inputs and outputs as for moe_forward. A configuration whose
+ * moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES is refused with
+ * MOE_ERR_WORKSPACE_TOO_SMALL before anything is launched (64 MiB holds a
+ * decode batch of up to 64 tokens, or an MXFP4 batch of about 400 tokens, at
+ * H 4096, I 2048, 256 experts, top-6). Every call on one device shares that
+ * device's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller. The array keeps the
+ * last call's contents; no kernel depends on its initial contents. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* router_w, const float* router_bias,
+                        const uint8_t* w13, const uint8_t* w13_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                        float* out, int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* moe_forward that also copies the intermediates named in taps and records
  * the stage events (NULL taps = moe_forward), for the fixed-token and hash
  * checks of the gfx90a paper (abstract). The copies are extra kernels after
