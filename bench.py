@@ -453,6 +453,33 @@ def streaming_read_gbs(torch, SD, gib: int = 8, reps: int = 5) -> float:
     return (gib << 30) / (ms / 1e3) / 1e9
 
 
+def mfma_probe(torch, SD, iters: int = 40000) -> dict:
+    """Scaled FP4 MFMA issue rate on random operands, with one and two waves
+    per SIMD: TFLOP/s from events and the shader clock measured in-kernel
+    (s_memtime cycles over the 100 MHz s_memrealtime)."""
+    res = {}
+    for per_simd in (1, 2):
+        blocks = 256 * per_simd  # 4 waves a workgroup: one per SIMD
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        clocks = torch.empty(blocks * 8, dtype=torch.int64, device="cuda")
+        SD.mfma_probe(blocks, 100, out, clocks)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        SD.mfma_probe(blocks, iters, out, clocks)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        flops = blocks * 4 * iters * 8 * 131072.0
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        mhz = c[:, 0] / (c[:, 1] / 100.0)
+        res[f"waves_per_simd_{per_simd}"] = {
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1), "ms": round(ms, 3),
+            "shader_mhz_median": round(float(np.median(mhz)), 1),
+            "cycles_per_mfma_per_simd": round(float(np.median(c[:, 0])) / (iters * 8 * per_simd), 2)}
+    return res
+
+
 def leg_summary(v: dict) -> dict:
     return {"tokens_per_s": round(v["tokens_per_s"], 1), "ms_per_step": round(v["ms_per_step"], 5),
             "step_ms": v["step_ms"],
@@ -480,6 +507,8 @@ def main():
                     help="comma-separated legs to run after the headline workload ('' for none)")
     ap.add_argument("--no-legs", action="store_true", help="run the headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the FP4 MFMA rate / shader clock probe and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -503,6 +532,9 @@ def main():
     from fp4_routed_mixture_amd import binding as B
     from fp4_routed_mixture_amd import synth as S
     from fp4_routed_mixture_amd import synth_device as SD
+    if args.mfma_probe:
+        print(json.dumps(mfma_probe(torch, SD)))
+        return
     B.lib()
     ev = HipEvents()
     w = S.WORKLOADS[args.workload]

@@ -1,7 +1,9 @@
 """Build the gfx950 HIP libraries in-tree with hipcc.
 
   libfp4moe.so        the routed-MoE layer (csrc/*.hip except synth.hip)
-  libfp4moe_synth.so  the device side of the seeded input generator
+  libfp4moe_synth.so  test and benchmark support: the device side of the seeded
+                      input generator, the streaming-read and FP4 MFMA probes,
+                      and a hook evaluating the kernels' exp and sigmoid
 
 Every kernel is compiled for gfx950 only, without fast-math, with fp
 contraction off (fused multiply-adds are written explicitly where the

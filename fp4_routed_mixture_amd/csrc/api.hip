@@ -62,8 +62,9 @@ int check_shape(const moe_config* c) {
 
 // Workspace plan of one layer call.
 struct Plan {
-  int block_m, P, cap, max_tiles;
-  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, a, aq, as, y, total;
+  int block_m, P, cap, max_tiles, max_wide;
+  size_t logits, ids, w, xq, xs, counts, offsets, sorted, pos, tiles, ntiles, wide, nwide, sort_scratch, a, aq, as, y,
+      total;
 };
 
 Plan make_plan(const moe_config* c) {
@@ -74,6 +75,8 @@ Plan make_plan(const moe_config* c) {
   p.P = T * k;
   p.cap = p.P + (E < p.P ? E : p.P) * (p.block_m - 1);
   p.max_tiles = p.cap / p.block_m;
+  // wide tiles of the prefill GEMMs: ceil(tiles / 2) per expert with pairs
+  p.max_wide = mx ? (p.max_tiles + (E < p.P ? E : p.P)) / 2 + 1 : 0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -91,6 +94,8 @@ Plan make_plan(const moe_config* c) {
   p.pos = take((size_t)p.P * 4);
   p.tiles = take((size_t)(p.max_tiles + 1) * 4);
   p.ntiles = take(4);
+  p.wide = take((size_t)(p.max_wide + 1) * 4);
+  p.nwide = take(4);
   p.sort_scratch = take(moe_k_sort_scratch_bytes(p.P, E));
   p.a = take(mx ? 0 : (size_t)p.cap * I * 4);
   p.aq = take(mx ? (size_t)p.cap * I / 2 : (size_t)p.cap * 2 * I);
@@ -222,6 +227,7 @@ int moe_sort(const moe_config* cfg, int32_t block_m, const int32_t* topk_ids, in
   if (scratch && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
   if (workspace_bytes < scratch) return MOE_ERR_WORKSPACE_TOO_SMALL;
   MOE_TRY(moe_k_sort(topk_ids, P, cfg->E, block_m, counts, offsets, sorted_pairs, pair_pos, tile_expert, n_tiles,
+                     nullptr, nullptr,
                      workspace, (hipStream_t)stream));
   return MOE_OK;
 }
@@ -303,6 +309,8 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   int32_t* pos = at<int32_t>(workspace, p.pos);
   int32_t* tiles = at<int32_t>(workspace, p.tiles);
   int32_t* ntiles = at<int32_t>(workspace, p.ntiles);
+  int32_t* wide = mx ? at<int32_t>(workspace, p.wide) : nullptr;
+  int32_t* nwide = mx ? at<int32_t>(workspace, p.nwide) : nullptr;
   void* sort_scratch = at<void>(workspace, p.sort_scratch);
   float* a = at<float>(workspace, p.a);
   uint8_t* aq = at<uint8_t>(workspace, p.aq);
@@ -328,7 +336,7 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
     MOE_TRY(mark(2 * MOE_STAGE_TOPK));
     if (route_sorts)
       MOE_TRY(moe_k_route_sort_small(logits, router_bias, T, E, k, p.block_m, ids, w, counts, offsets, sorted, pos,
-                                     tiles, ntiles, s));
+                                     tiles, ntiles, wide, nwide, s));
     else
       MOE_TRY(moe_k_topk_quant(cfg->x_dtype, logits, router_bias, x, T, H, E, k, qr ? 0 : 1, mx, ids, w, xq,
                                (uint8_t*)xs, s));
@@ -353,18 +361,21 @@ int forward_impl(const moe_config* cfg, const void* x, const float* router_w, co
   // sort
   MOE_TRY(mark(2 * MOE_STAGE_SORT));
   if (!route_sorts)
-    MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, sort_scratch, s));
+    MOE_TRY(moe_k_sort(ids, P, E, p.block_m, counts, offsets, sorted, pos, tiles, ntiles, wide, nwide, sort_scratch,
+                       s));
   MOE_TRY(mark(2 * MOE_STAGE_SORT + 1));
   // expert GEMMs
   if (mx) {
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP));
-    MOE_TRY(moe_k_prefill_gemm(1, canon, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, ntiles, p.max_tiles, H,
+    MOE_TRY(moe_k_prefill_gemm(1, canon, w13, w13_scale, xq, (const uint8_t*)xs, sorted, tiles, wide, nwide,
+                               p.max_wide, H,
                                I / 32, k, P, 1, aq, (uint8_t*)as, nullptr, I, s));
     MOE_TRY(mark(2 * MOE_STAGE_GATE_UP + 1));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT));
     MOE_TRY(mark(2 * MOE_STAGE_REQUANT + 1));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN));
-    MOE_TRY(moe_k_prefill_gemm(0, canon, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, ntiles, p.max_tiles, I,
+    MOE_TRY(moe_k_prefill_gemm(0, canon, w2, w2_scale, aq, (const uint8_t*)as, sorted, tiles, wide, nwide,
+                               p.max_wide, I,
                                H / 32, k, P, 0, nullptr, nullptr, y, H, s));
     MOE_TRY(mark(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(mark(2 * MOE_STAGE_COMBINE));

@@ -40,15 +40,17 @@ inline hipError_t once_per_device(std::atomic<bool>* done, F set) {
 // Inputs above the largest z with a finite result give +inf, inputs below
 // ln(2^-150) give 0.
 // ---------------------------------------------------------------------------
+// The polynomial path is evaluated for every input and the out-of-range
+// results are selected afterwards (no branches: the three range tests as
+// branches cost more than the polynomial). For z outside the range the
+// evaluated value is discarded, so the result is the same for every input.
 __device__ __forceinline__ float exp_fixed(float z) {
   const float kLog2e = 0x1.715476p+0f;
   const float kLn2Hi = 0x1.62e4p-1f;
   const float kLn2Lo = 0x1.7f7d1cp-20f;
-  if (z != z) return z;
-  if (z > 0x1.62e42ep+6f) return __builtin_inff();
-  if (z < -0x1.9fe36ap+6f) return 0.0f;
-  float n = __builtin_rintf(z * kLog2e);
-  float r = __builtin_fmaf(-n, kLn2Hi, z);
+  const float zc = __builtin_fminf(__builtin_fmaxf(z, -0x1.9fe36ap+6f), 0x1.62e42ep+6f);  // keeps n in range
+  float n = __builtin_rintf(zc * kLog2e);
+  float r = __builtin_fmaf(-n, kLn2Hi, zc);
   r = __builtin_fmaf(-n, kLn2Lo, r);
   float p = 0x1.a01a02p-13f;                 // 1/7!
   p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
@@ -58,7 +60,10 @@ __device__ __forceinline__ float exp_fixed(float z) {
   p = __builtin_fmaf(p, r, 0.5f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  return __builtin_ldexpf(p, (int)n);
+  float e = __builtin_ldexpf(p, (int)n);
+  e = z > 0x1.62e42ep+6f ? __builtin_inff() : e;
+  e = z < -0x1.9fe36ap+6f ? 0.0f : e;
+  return z != z ? z : e;
 }
 
 // IEEE division (hipcc lowers '/' on fp32 to the correctly rounded sequence;

@@ -28,16 +28,19 @@ hipError_t moe_k_finish_logits(const float* partial, const float* bias, int T, i
 int moe_k_route_sort_fits(int T, int H, int E, int K);
 hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T, int E, int K, int block_m,
                                   int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
-                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, hipStream_t st);
+                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, int32_t* wide,
+                                  int32_t* n_wide, hipStream_t st);
 hipError_t moe_k_topk_quant(int x_dtype, const float* partial, const float* bias, const void* x, int T, int H, int E,
                             int K, int quant, int mx, int32_t* ids, float* w, uint8_t* xq, uint8_t* xs,
                             hipStream_t st);
 
-// sort.hip
+// sort.hip. wide / n_wide (nullable): the prefill GEMMs' list of wide tiles,
+// (first tile << 1) | (a second tile of the same expert follows), and its
+// length: at most (n_tiles + E) / 2 + 1 entries.
 size_t moe_k_sort_scratch_bytes(int P, int E);
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
-                      int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      hipStream_t st);
+                      int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, int32_t* wide,
+                      int32_t* n_wide, void* scratch, hipStream_t st);
 
 hipError_t moe_k_copy_routing(const int32_t* ids_in, const float* w_in, int P, int E, int32_t* ids, float* w,
                               hipStream_t st);
@@ -66,10 +69,13 @@ hipError_t moe_k_decode_down(int canon, const uint8_t* wq, const uint8_t* wsc, c
 
 // gemm_prefill.hip
 int moe_k_prefill_block_m();
+// (wide / n_wide: the sort's wide-tile list; max_wide: the grid's bound on its
+// length)
 hipError_t moe_k_prefill_gemm(int gate_up, int canon, const uint8_t* wq, const uint8_t* wsc, const uint8_t* act_codes,
                               const uint8_t* act_scales, const int32_t* sorted, const int32_t* tile_expert,
-                              const int32_t* n_tiles, int max_tiles, int K, int NT, int top_k, int P,
-                              int rows_are_tokens, uint8_t* aq, uint8_t* as, float* y, int out_n, hipStream_t st);
+                              const int32_t* wide, const int32_t* n_wide, int max_wide, int K, int NT, int top_k,
+                              int P, int rows_are_tokens, uint8_t* aq, uint8_t* as, float* y, int out_n,
+                              hipStream_t st);
 
 // combine.hip
 hipError_t moe_k_combine(const float* y, const float* w, int T, int H, int K, float* out, hipStream_t st);

@@ -653,7 +653,8 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
     const float* __restrict__ partial, const float* __restrict__ bias, int T, int E, int K, int block_m,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
-    int32_t* __restrict__ tile_expert, int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ n_tiles, int32_t* __restrict__ wide,
+    int32_t* __restrict__ n_wide) {
   extern __shared__ int smem[];
   __shared__ int ids_lds[moe::SB];
   __shared__ int sel_id[16][16];
@@ -704,6 +705,7 @@ __global__ __launch_bounds__(1024) void route_sort_small_kernel(
   for (int e = tid; e < E; e += blockDim.x) counts[e] = tot[e];
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+  if (wide) moe::write_wide_tiles(offs, E, block_m, tmp, wide, n_wide);
 }
 
 // ---------------------------------------------------------------------------
@@ -962,7 +964,8 @@ int moe_k_route_sort_fits(int T, int H, int E, int K) { return moe_k_router_slic
 
 hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T, int E, int K, int block_m,
                                   int32_t* ids, float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
-                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, hipStream_t st) {
+                                  int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, int32_t* wide,
+                                  int32_t* n_wide, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (T * K > moe::SB || K > 16 || E > 1024 || T * E > RS_MAX_TE) return hipErrorInvalidValue;
   // above 64 KB of LDS a kernel must opt in (gfx950: 160 KB per workgroup)
@@ -975,7 +978,7 @@ hipError_t moe_k_route_sort_small(const float* partial, const float* bias, int T
   const int P = T * K, W = (P + 31) / 32;
   const size_t lds = (size_t)(std::max(T * E, E * W) + E + E + 1 + 1024) * 4;
   route_sort_small_kernel<<<1, 1024, lds, st>>>(partial, bias, T, E, K, block_m, ids, w, counts, offsets, sorted, pos,
-                                                tile_expert, n_tiles);
+                                                tile_expert, n_tiles, wide, n_wide);
   return hipGetLastError();
 }
 

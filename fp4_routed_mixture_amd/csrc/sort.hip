@@ -27,7 +27,8 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
                                                           int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ n_tiles) {
+                                                          int32_t* __restrict__ n_tiles, int32_t* __restrict__ wide,
+                                                          int32_t* __restrict__ n_wide) {
   extern __shared__ int smem[];
   const int W = (P + 31) >> 5;
   uint32_t* mask = reinterpret_cast<uint32_t*>(smem);  // E * W
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
   for (int e = tid; e < E; e += blockDim.x) counts[e] = tot[e];
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+  if (wide) moe::write_wide_tiles(offs, E, block_m, tmp, wide, n_wide);
 }
 
 // Large P, step 1: per block local ranks and per-expert block counts.
@@ -78,7 +80,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ sorted,
                                                          int32_t* __restrict__ tile_expert,
-                                                         int32_t* __restrict__ n_tiles) {
+                                                         int32_t* __restrict__ n_tiles, int32_t* __restrict__ wide,
+                                                         int32_t* __restrict__ n_wide) {
   extern __shared__ int smem[];
   int* tot = smem;            // E
   int* offs = tot + E;        // E + 1
@@ -152,6 +155,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int nblocks, int P, int
   }
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
   moe::write_tiles_and_padding(tot, offs, E, P, block_m, sorted, tile_expert, n_tiles);
+  if (wide) moe::write_wide_tiles(offs, E, block_m, tmp, wide, n_wide);
 }
 
 // Routing given by a caller: ids clamped into [0, E), weights copied.
@@ -194,8 +198,8 @@ size_t moe_k_sort_scratch_bytes(int P, int E) {
 }
 
 hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* counts, int32_t* offsets,
-                      int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, void* scratch,
-                      hipStream_t st) {
+                      int32_t* sorted, int32_t* pos, int32_t* tile_expert, int32_t* n_tiles, int32_t* wide,
+                      int32_t* n_wide, void* scratch, hipStream_t st) {
   // gfx950 has 160 KB of LDS per workgroup; above 64 KB a kernel must opt in
   static std::atomic<bool> lds_opt_in[moe::kMaxDevices];
   const hipError_t eo = moe::once_per_device(lds_opt_in, [] {
@@ -210,7 +214,8 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
   if (eo != hipSuccess) return eo;
   if (P <= moe::SB) {
     size_t lds = (size_t)(E * ((P + 31) / 32) + E + E + 1 + 1024) * 4;
-    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles);
+    sort_small_kernel<<<1, 1024, lds, st>>>(ids, P, E, block_m, counts, offsets, sorted, pos, tile_expert, n_tiles,
+                                            wide, n_wide);
     return hipGetLastError();
   }
   int nb = (P + moe::SB - 1) / moe::SB;
@@ -222,10 +227,10 @@ hipError_t moe_k_sort(const int32_t* ids, int P, int E, int block_m, int32_t* co
   const size_t scan_lds = (size_t)(E + E + 1 + 1024) * 4, hist_lds = (size_t)nb * E * 4;
   if (scan_lds + hist_lds <= kScanLdsMax)
     sort_scan_kernel<true><<<1, 1024, scan_lds + hist_lds, st>>>(nb, P, E, block_m, block_hist, counts, offsets,
-                                                                 sorted, tile_expert, n_tiles);
+                                                                 sorted, tile_expert, n_tiles, wide, n_wide);
   else
     sort_scan_kernel<false><<<1, 1024, scan_lds, st>>>(nb, P, E, block_m, block_hist, counts, offsets, sorted,
-                                                       tile_expert, n_tiles);
+                                                       tile_expert, n_tiles, wide, n_wide);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   sort_scatter_kernel<<<(P + 255) / 256, 256, 0, st>>>(ids, P, E, local_rank, block_hist, sorted, pos);

@@ -90,4 +90,34 @@ __device__ inline void write_tiles_and_padding(const int* counts, const int* off
   if (tid == 0) *n_tiles = offs[E] / block_m;
 }
 
+// Wide tiles of the prefill GEMMs: expert e's padded segment holds
+// n_e = (offs[e + 1] - offs[e]) / block_m sort tiles, covered in order by
+// ceil(n_e / 2) wide tiles of two (the last one of an odd n_e holds one).
+// wide[w] = (first sort tile << 1) | (1 if a second tile follows);
+// *n_wide = their number. blockDim.x == 1024, E <= 1024; tmp: 32 LDS ints,
+// free (scan_offsets leaves them so after its last barrier).
+__device__ inline void write_wide_tiles(const int* offs, int E, int block_m, int* tmp, int32_t* __restrict__ wide,
+                                        int32_t* __restrict__ n_wide) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n = 0, m = 0;
+  if (tid < E) {
+    n = (offs[tid + 1] - offs[tid]) / block_m;
+    m = (n + 1) >> 1;
+  }
+  const int v = wave_incl_scan(m);
+  if (lane == 63) tmp[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    const int t = wave_incl_scan(lane < 16 ? tmp[lane] : 0);
+    if (lane < 16) tmp[16 + lane] = t - tmp[lane];
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int base = v - m + tmp[16 + wave];
+    const int t0 = offs[tid] / block_m;
+    for (int i = 0; i < m; ++i) wide[base + i] = ((t0 + 2 * i) << 1) | (2 * i + 1 < n ? 1 : 0);
+    if (tid == E - 1) *n_wide = base + m;
+  }
+}
+
 }  // namespace moe

@@ -4,10 +4,17 @@
 // stream with key K is mix(K + (i + 1) * 0x9E3779B97F4A7C15), each output
 // gives eight little-endian bytes; a scale byte is 121 + (byte mod 5).
 // Used to place the 43-layer stack (about 147 GB) in HBM without a host copy.
-// The same benchmark-support library holds a plain streaming-read probe, the
-// practical HBM read ceiling that the weight-streaming kernels are set beside.
+// For the tests it also evaluates the layer's own device exp and sigmoid
+// (common.h) on an array, so that their bits can be compared with the CPU
+// oracle's over the whole input range.
+// The same benchmark-support library holds two probes: a plain streaming read
+// (the practical HBM read ceiling that the weight-streaming kernels are set
+// beside) and a scaled-FP4 MFMA issue loop on random operands with the shader
+// clock read in-kernel (the matrix rate the chip sustains under that load).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "common.h"
 
 namespace {
 
@@ -57,9 +64,81 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   }
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Eight independent accumulators per wave, each fed one
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4, 131,072 FLOP) per iteration
+// on operands drawn from a per-lane xorshift stream (random E2M1 codes, scale
+// 1); every wave records its shader-clock and 100 MHz constant-clock deltas.
+__global__ __launch_bounds__(256) void mfma_fp4_probe_kernel(int iters, uint32_t seed, float* __restrict__ out,
+                                                             uint64_t* __restrict__ clocks) {
+  uint32_t st = seed ^ (blockIdx.x * 256u + threadIdx.x) * 0x9E3779B9u;
+  auto next = [&]() {
+    st ^= st << 13;
+    st ^= st >> 17;
+    st ^= st << 5;
+    return (int)st;
+  };
+  i32x8 a[2], b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[u][k] = k < 4 ? next() : 0;
+      b[u][k] = k < 4 ? next() : 0;
+    }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = (f32x16){};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 1], b[(j >> 1) & 1], acc[j], 4, 4, 0, 127, 0,
+                                                                127);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[j][v];
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+  if ((threadIdx.x & 63) == 0) {
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    clocks[2 * w] = t1 - t0;
+    clocks[2 * w + 1] = r1 - r0;
+  }
+}
+
+__global__ void exp_sigmoid_kernel(const float* __restrict__ z, int n, float* __restrict__ e, float* __restrict__ s) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  e[i] = moe::exp_fixed(z[i]);
+  s[i] = moe::sigmoid_fixed(z[i]);
+}
+
 }  // namespace
 
 extern "C" {
+
+// exp_fixed and sigmoid_fixed of the layer's kernels on n values (device arrays).
+int synth_exp_sigmoid(const float* z, int n, float* e, float* s, void* stream) {
+  if (n < 0 || (n && (!z || !e || !s))) return 1;
+  if (n == 0) return 0;
+  exp_sigmoid_kernel<<<(n + 255) / 256, 256, 0, (hipStream_t)stream>>>(z, n, e, s);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The FP4 MFMA probe: blocks workgroups of 4 waves, iters iterations of 8
+// MFMAs per wave. out: blocks * 256 floats; clocks: blocks * 4 * 2 uint64
+// (shader-clock and 100 MHz-clock deltas of each wave).
+int synth_mfma_probe(int blocks, int iters, void* out, void* clocks, void* stream) {
+  if (blocks < 1 || iters < 1 || !out || !clocks) return 1;
+  mfma_fp4_probe_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out, (uint64_t*)clocks);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // Streaming read of nbytes (multiple of 16, 16-byte aligned) at src with
 // `blocks` workgroups of 256 threads; sink receives `blocks` 16-byte words.

@@ -32,6 +32,10 @@ def slib():
         L.synth_fill.argtypes = [C.c_int, C.c_int, C.c_int, C.c_uint64, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
         L.synth_stream_key.restype = C.c_uint64
         L.synth_stream_key.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.synth_exp_sigmoid.restype = C.c_int
+        L.synth_exp_sigmoid.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.synth_mfma_probe.restype = C.c_int
+        L.synth_mfma_probe.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         L.synth_stream_read.restype = C.c_int
         L.synth_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
         _slib = L
@@ -117,3 +121,22 @@ def stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor) -> None:
                                   torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_stream_read failed ({rc})")
+
+
+def mfma_probe(blocks: int, iters: int, out: torch.Tensor, clocks: torch.Tensor) -> None:
+    """Enqueue the FP4 MFMA rate probe (a benchmark ceiling, not part of the
+    layer): out holds blocks * 256 floats, clocks blocks * 8 int64."""
+    rc = slib().synth_mfma_probe(blocks, iters, out.data_ptr(), clocks.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_mfma_probe failed ({rc})")
+
+
+def exp_sigmoid(z: torch.Tensor):
+    """The layer kernels' own fp32 exp and sigmoid of z (a test hook)."""
+    e, s = torch.empty_like(z), torch.empty_like(z)
+    rc = slib().synth_exp_sigmoid(z.data_ptr(), z.numel(), e.data_ptr(), s.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_exp_sigmoid failed ({rc})")
+    return e, s

@@ -300,3 +300,24 @@ def test_topk_ties_go_to_lower_index(T, E, k):
     # with every logit equal to its bias, the selection is the stable order
     order = sorted(range(E), key=lambda e: (-float(b_h[e]), e))[:k]
     assert all(list(r) == order for r in ids_o.tolist())
+
+
+def test_device_exp_sigmoid_bitexact():
+    """The kernels' fp32 exp and sigmoid (evaluated for every input, the
+    out-of-range results selected afterwards) equal the oracle's bit for bit
+    on 2^24 inputs spread over [-110, 95] plus the range edges, their
+    neighbours, +-0, +-inf, NaN and subnormals."""
+    rng = np.random.default_rng(77)
+    z = np.concatenate([
+        np.linspace(-110.0, 95.0, 1 << 23, dtype=np.float32),
+        rng.uniform(-110.0, 95.0, 1 << 23).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45, 1e-38, -1e-38, 88.72283, -103.97208],
+                 np.float32)])
+    edges = np.array([float.fromhex("0x1.62e42ep+6"), -float.fromhex("0x1.9fe36ap+6")], np.float32)
+    z = np.concatenate([z, np.nextafter(edges, np.float32(np.inf)), np.nextafter(edges, np.float32(-np.inf)), edges])
+    e, s = SD.exp_sigmoid(torch.from_numpy(z).cuda())
+    torch.cuda.synchronize()
+    e, s = e.cpu().numpy(), s.cpu().numpy()
+    ref_e, ref_s = oracle.expf(z), oracle.sigmoidf(z)
+    assert np.array_equal(e.view(np.uint32), ref_e.view(np.uint32)), f"{(e.view(np.uint32) != ref_e.view(np.uint32)).sum()} exp differ"
+    assert np.array_equal(s.view(np.uint32), ref_s.view(np.uint32)), f"{(s.view(np.uint32) != ref_s.view(np.uint32)).sum()} sigmoid differ"
