@@ -29,7 +29,11 @@ Generators:
     eight bytes, little-endian. A code byte is that byte (two E2M1 codes,
     uniform over all 16 values); a scale byte is 121 + (byte mod 5), i.e.
     2^-6 .. 2^-2. The stream key is mix((seed << 40) | (layer << 16) | tensor)
-    with tensor 0 = W13 codes, 1 = W13 scales, 2 = W2 codes, 3 = W2 scales.
+    with tensor 0 = W13 codes, 1 = W13 scales, 2 = W2 codes, 3 = W2 scales,
+    4 = dense FP8 codes, 5 = dense FP8 scales.
+  * Dense FP8 (E4M3) weight codes: the stream's bytes with the two NaN codes
+    (0x7f, 0xff) replaced by their neighbours 0x7e, 0xfe (+-448); scales as
+    above.
     A device kernel (csrc/synth.hip) implements the same definition so the
     43-layer stack (about 147 GB) can be generated in HBM; a GPU test checks
     that both produce the same bytes.
@@ -49,6 +53,8 @@ TENSOR_W13_CODES = 0
 TENSOR_W13_SCALES = 1
 TENSOR_W2_CODES = 2
 TENSOR_W2_SCALES = 3
+TENSOR_DENSE_CODES = 4
+TENSOR_DENSE_SCALES = 5
 
 ACT_INT8 = 0
 ACT_MXFP4 = 1
@@ -157,6 +163,43 @@ def all_expert_weights(w: Workload, layer: int = 0):
     w2 = code_bytes(w.seed, layer, TENSOR_W2_CODES, 0, E * H * I // 2).reshape(E, H, I // 2)
     w2s = scale_bytes(w.seed, layer, TENSOR_W2_SCALES, 0, E * H * I // 32).reshape(E, H, I // 32)
     return w13, w13s, w2, w2s
+
+
+@dataclasses.dataclass(frozen=True)
+class DenseWorkload:
+    """A block-scaled FP8 dense projection: M tokens, K = input features (the
+    hidden size), N = output features."""
+    name: str
+    M: int
+    K: int
+    N: int
+    x_dtype: int
+    seed: int
+
+
+DENSE_WORKLOADS = {
+    "dense_tiny": DenseWorkload("dense_tiny", 4, 256, 256, X_F32, 0),
+    "dense_t32": DenseWorkload("dense_t32", 32, 4096, 4096, X_BF16, 5),
+    "dense_t4604": DenseWorkload("dense_t4604", 4604, 4096, 4096, X_BF16, 6),
+    "dense_t16384": DenseWorkload("dense_t16384", 16384, 4096, 4096, X_BF16, 7),
+    "dense_t4604_n1536": DenseWorkload("dense_t4604_n1536", 4604, 4096, 1536, X_BF16, 8),
+}
+
+
+def dense_weights(w: DenseWorkload):
+    """(codes [N][K] u8 E4M3 without NaN codes, E8M0 scales [N][K/32] u8)."""
+    raw = code_bytes(w.seed, 0, TENSOR_DENSE_CODES, 0, w.N * w.K)
+    nan = (raw & np.uint8(0x7F)) == np.uint8(0x7F)
+    raw[nan] ^= np.uint8(1)
+    sc = scale_bytes(w.seed, 0, TENSOR_DENSE_SCALES, 0, w.N * w.K // 32)
+    return raw.reshape(w.N, w.K), sc.reshape(w.N, w.K // 32)
+
+
+def dense_activations(w: DenseWorkload, M: int | None = None) -> np.ndarray:
+    """x [M][K]: fp32 N(0, 1), or its nearest-even bf16 bit patterns."""
+    M = w.M if M is None else M
+    x = np.random.default_rng([w.seed, 0, 0]).standard_normal((M, w.K), dtype=np.float32)
+    return f32_to_bf16_bits(x) if w.x_dtype == X_BF16 else x
 
 
 # --------------------------------------------------------------------------

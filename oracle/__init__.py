@@ -17,6 +17,11 @@ something other than itself):
                             scale-exponent doubling; permutation
                             equivariance; identical experts; zero weights
   rmsnorm                   float64 RMS within its error bound
+  e4m3_table, quant_mxfp8   torch's independent float8_e4m3fn conversion
+                            (decode of all codes, nearest-even rounding in
+                            range); brute-force grid search; saturation
+  dense_mxfp8               numpy float64 matmul of the dequantized operands;
+                            one-hot closed forms; scale-exponent doubling
 """
 from __future__ import annotations
 
@@ -83,6 +88,11 @@ def lib():
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, f32p,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.or_rmsnorm.argtypes = [C.c_int, C.c_int, f32p, f32p]
+        L.or_e4m3_value.restype = C.c_float
+        L.or_e4m3_value.argtypes = [C.c_int]
+        L.or_quant_mxfp8.argtypes = [C.c_int, C.c_int, f32p, u8p, u8p]
+        f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+        L.or_dense_mxfp8.argtypes = [C.c_int, C.c_int, C.c_int, u8p, u8p, u8p, u8p, f32p, C.c_void_p]
         L.or_num_threads.restype = C.c_int
         L.or_set_num_threads.argtypes = [C.c_int]
     return _lib
@@ -318,6 +328,43 @@ def moe_layer_routed(x, ids, w, experts, act_mode: int, intermediates: bool = Fa
     res = {"out": out}
     res.update(inter)
     return res
+
+
+# ------------------------------------------------------------ dense FP8 ---
+def e4m3_table() -> np.ndarray:
+    return np.array([lib().or_e4m3_value(c) for c in range(256)], np.float32)
+
+
+def quant_mxfp8(v):
+    """MXFP8 quantization per 32 along K: (codes [R][K] u8, E8M0 [R][K/32] u8)."""
+    v = _f32(v)
+    R, K = v.shape
+    assert K % 32 == 0
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty((R, K // 32), np.uint8)
+    lib().or_quant_mxfp8(R, K, v, codes, scales)
+    return codes, scales
+
+
+def dense_mxfp8(xq, xs, wq, ws, bound: bool = False):
+    """Y = X W^T for MXFP8 X [M][K] and W [N][K] (exact block sums, float64
+    accumulation, one rounding to fp32); with bound, also the float64
+    sum of |products| times scales (the fp32 error budget's base)."""
+    xq, xs = np.ascontiguousarray(xq, np.uint8), np.ascontiguousarray(xs, np.uint8)
+    wq, ws = np.ascontiguousarray(wq, np.uint8), np.ascontiguousarray(ws, np.uint8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    out = np.empty((M, N), np.float32)
+    ab = np.empty((M, N), np.float64) if bound else None
+    lib().or_dense_mxfp8(M, N, K, xq, xs, wq, ws, out, _ptr(ab))
+    return (out, ab) if bound else out
+
+
+def dense_fp8(x, wq, ws, bound: bool = False):
+    """The projection of x (fp32, or bf16 bit patterns): MXFP8 quantization of
+    x per token, then dense_mxfp8."""
+    xq, xs = quant_mxfp8(x_to_f32(x))
+    return dense_mxfp8(xq, xs, wq, ws, bound)
 
 
 def rmsnorm(x):

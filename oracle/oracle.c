@@ -621,6 +621,111 @@ int or_moe_layer_routed(const or_config* c, const void* x, const int32_t* ids, c
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block-scaled FP8 dense projection (the model's FP8 dense projections: the  */
+/* gfx90a paper, abstract; FP8 block quantization: the gfx1201 blog, What we  */
+/* set out to do). Format (reading; the pages name no layout): OCP MX v1.0    */
+/* MXFP8, E4M3 elements with one E8M0 scale per 32 consecutive elements      */
+/* along K, for the weights [N][K] and for the activations quantized per     */
+/* token.                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 (OCP FP8, no infinities): bit 7 sign, bits 6..3 exponent (bias 7),
+ * bits 2..0 mantissa; exponent 0 is subnormal (m * 2^-9); exponent 15 with
+ * mantissa 7 is NaN. The largest finite magnitude is 1.75 * 2^8 = 448. */
+float or_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    float mag = (e == 0) ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest E4M3 magnitude code (0..126) for a >= 0: a scan over the finite
+ * magnitudes, ties to the code whose mantissa bit 0 is clear; anything above
+ * the largest magnitude saturates to 448 (code 126). */
+static int e4m3_nearest_mag(float a)
+{
+    if (a >= 448.0f) return 126;
+    int best = 0;
+    float bestd = INFINITY;
+    for (int c = 0; c < 127; ++c) {
+        float d = fabsf(a - or_e4m3_value(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* MXFP8 per block of 32 along K: the shared scale exponent is
+ * floor(log2 amax) - 8 (8 = the largest E4M3 exponent), stored biased by 127
+ * and clamped to [0, 254]; elements are scaled exactly by 2^(127 - e),
+ * rounded to the nearest E4M3 value with ties to even and saturated at 448.
+ * The code's sign bit is the element's sign bit. A block with amax = 0 gets
+ * scale byte 0 and codes 0. codes: [R][K]; scales: [R][K/32]. */
+void or_quant_mxfp8(int R, int K, const float* v, uint8_t* codes, uint8_t* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < R; ++r)
+        for (int b = 0; b < K / 32; ++b) {
+            const float* blk = v + (size_t)r * K + 32 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(blk[i]));
+            int e = 0;
+            if (amax > 0.0f) {
+                int ex;
+                frexpf(amax, &ex); /* floor(log2 amax) = ex - 1 */
+                e = (ex - 1) - 8 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            scales[(size_t)r * (K / 32) + b] = (uint8_t)e;
+            for (int i = 0; i < 32; ++i) {
+                int code = 0;
+                if (amax > 0.0f) {
+                    float vs = ldexpf(blk[i], 127 - e);
+                    code = e4m3_nearest_mag(fabsf(vs)) | (signbit(vs) ? 0x80 : 0);
+                }
+                codes[(size_t)r * K + 32 * b + i] = (uint8_t)code;
+            }
+        }
+}
+
+/* Y[m][n] = sum_b 2^(ex[m][b] + ew[n][b] - 254) * sum_{k in b} x_k w_k with the
+ * E4M3 values x, w. The products are exact in float64 and so is each block
+ * sum (at most 32 products spanning under 48 significant bits); the block
+ * terms are added in float64 in ascending b and the result rounded once to
+ * fp32. absbound (nullable) receives sum_b 2^(...) sum_k |x_k w_k| in float64:
+ * any fp32 evaluation that adds the K products in some order stays within
+ * K * 2^-24 * absbound of the exact value. x: codes [M][K], scales [M][K/32];
+ * w: codes [N][K], scales [N][K/32]. */
+void or_dense_mxfp8(int M, int N, int K, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                    const uint8_t* ws, float* out, double* absbound)
+{
+    double tab[256];
+    for (int c = 0; c < 256; ++c) tab[c] = (double)or_e4m3_value(c);
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0, bound = 0.0;
+            for (int b = 0; b < K / 32; ++b) {
+                double bs = 0.0, ba = 0.0;
+                for (int i = 0; i < 32; ++i) {
+                    double p = tab[xq[(size_t)m * K + 32 * b + i]] * tab[wq[(size_t)n * K + 32 * b + i]];
+                    bs += p;
+                    ba += fabs(p);
+                }
+                double sc = ldexp(1.0, (int)xs[(size_t)m * (K / 32) + b] + (int)ws[(size_t)n * (K / 32) + b] - 254);
+                acc += bs * sc;
+                bound += ba * sc;
+            }
+            out[(size_t)m * N + n] = (float)acc;
+            if (absbound) absbound[(size_t)m * N + n] = bound;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* RMSNorm for the stacked-layer residual stream                             */
 /* ------------------------------------------------------------------------ */
 /* Unit-gain RMSNorm between stacked layers (x_{l+1} = x_l + moe(rmsnorm(x_l))):
