@@ -29,7 +29,8 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_wo
            "moe_prepacked_size", "moe_prepack", "moe_unpack", "moe_route", "moe_router_logits", "moe_sort",
            "moe_quantize",
            "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
-           "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps", "moe_forward_noalloc"]
+           "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps", "moe_forward_noalloc",
+           "moe_dense_fp8_workspace_size", "moe_dense_fp8_quantize", "moe_dense_fp8_gemm", "moe_dense_fp8_forward"]
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -48,6 +49,13 @@ class moe_config(C.Structure):
 
     def __repr__(self):
         return "moe_config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class moe_dense_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("M", "N", "K", "x_dtype")]
+
+    def __repr__(self):
+        return "moe_dense_config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
 class moe_taps(C.Structure):
@@ -70,6 +78,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
         cfgp = C.POINTER(moe_config)
+        dcfgp = C.POINTER(moe_dense_config)
         sig = {
             "moe_abi_version": (C.c_int, []),
             "moe_status_string": (C.c_char_p, [C.c_int]),
@@ -93,6 +102,10 @@ def lib():
             "moe_forward_stack": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_forward_stack_taps": (C.c_int, [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_forward_noalloc": (C.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "moe_dense_fp8_workspace_size": (C.c_int, [dcfgp, C.POINTER(sz)]),
+            "moe_dense_fp8_quantize": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
+            "moe_dense_fp8_gemm": (C.c_int, [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_dense_fp8_forward": (C.c_int, [dcfgp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -284,3 +297,30 @@ def moe_forward_stack_taps(cfg, x, layers, workspace, layer_taps, layer_out=None
                                         _p(layer_out), C.cast(tps, C.c_void_p), _p(workspace), workspace.numel(),
                                         _s(stream)), "moe_forward_stack_taps")
     return bm.value
+
+
+# ------------------------------------------------------------- dense FP8 --
+def make_dense_config(M, N, K, x_dtype=MOE_X_BF16) -> moe_dense_config:
+    return moe_dense_config(M, N, K, x_dtype)
+
+
+def moe_dense_fp8_workspace_size(cfg) -> int:
+    n = C.c_size_t(0)
+    _check(lib().moe_dense_fp8_workspace_size(C.byref(cfg), C.byref(n)), "moe_dense_fp8_workspace_size")
+    return n.value
+
+
+def moe_dense_fp8_quantize(rows, K, in_dtype, v, codes, scales, stream=None):
+    _check(lib().moe_dense_fp8_quantize(rows, K, in_dtype, _p(v), _p(codes), _p(scales), _s(stream)),
+           "moe_dense_fp8_quantize")
+
+
+def moe_dense_fp8_gemm(cfg, xq, xs, w, w_scale, y, workspace=None, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel()
+    _check(lib().moe_dense_fp8_gemm(C.byref(cfg), _p(xq), _p(xs), _p(w), _p(w_scale), _p(y), _p(workspace),
+                                    nbytes, _s(stream)), "moe_dense_fp8_gemm")
+
+
+def moe_dense_fp8_forward(cfg, x, w, w_scale, y, workspace, stream=None):
+    _check(lib().moe_dense_fp8_forward(C.byref(cfg), _p(x), _p(w), _p(w_scale), _p(y), _p(workspace),
+                                       workspace.numel(), _s(stream)), "moe_dense_fp8_forward")

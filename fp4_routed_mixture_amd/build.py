@@ -31,7 +31,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 LIB_SOURCES = ["api.hip", "prepack.hip", "route.hip", "sort.hip", "quant.hip",
-               "gemm_decode.hip", "gemm_prefill.hip", "combine.hip"]
+               "gemm_decode.hip", "gemm_prefill.hip", "gemm_dense.hip", "combine.hip"]
 
 
 def _compile(src: str) -> str:

@@ -555,3 +555,106 @@ int moe_residual_add(int64_t n, float* x, const float* y, void* stream) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ dense FP8 ----
+namespace {
+
+int check_dense(const moe_dense_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->x_dtype != MOE_X_F32 && c->x_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->M < 0 || c->M > (1 << 20)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (c->K < 128 || c->K > 32768 || c->K % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+  const int bn = moe_k_dense_block_n();
+  if (c->N < bn || c->N > 65536 || c->N % bn) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // token rows are addressed with 32-bit byte offsets
+  if ((uint64_t)c->M * c->K >= (1ull << 32)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+struct DensePlan {
+  size_t xq, xs, part, total;
+};
+
+DensePlan dense_plan(const moe_dense_config* c) {
+  DensePlan p;
+  p.xq = 0;
+  p.xs = up256((size_t)c->M * c->K);
+  p.part = p.xs + up256((size_t)c->M * (c->K / 32));
+  p.total = p.part + up256(moe_k_dense_partial_bytes(c->M, c->N, c->K));
+  return p;
+}
+
+int dense_gemm_checked(const moe_dense_config* c, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
+                       const uint8_t* w_scale, float* y, float* part, hipStream_t s) {
+  MOE_TRY(moe_k_dense_fp8_gemm(xq, xs, w, w_scale, c->M, c->N, c->K, y, part, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dense_fp8_workspace_size(const moe_dense_config* cfg, size_t* bytes) {
+  const int st = check_dense(cfg);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = dense_plan(cfg).total;
+  return MOE_OK;
+}
+
+int moe_dense_fp8_quantize(int32_t rows, int32_t K, int32_t in_dtype, const void* v, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (in_dtype != MOE_X_F32 && in_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows < 0 || K < 32 || K % 32 || K > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!v || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(v) || !aligned16(codes)) return MOE_ERR_ALIGNMENT;
+  MOE_TRY(moe_k_quant_mxfp8(in_dtype, v, rows, K, codes, scales, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_dense_fp8_gemm(const moe_dense_config* cfg, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
+                       const uint8_t* w_scale, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(cfg);
+  if (st) return st;
+  if (cfg->M == 0) return MOE_OK;
+  if (!xq || !xs || !w || !w_scale || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(w) || !aligned16(w_scale) || !aligned16(y))
+    return MOE_ERR_ALIGNMENT;
+  const DensePlan p = dense_plan(cfg);
+  const size_t part_bytes = moe_k_dense_partial_bytes(cfg->M, cfg->N, cfg->K);
+  if (part_bytes && (!workspace || workspace_bytes < p.total)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (part_bytes && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  const size_t ybytes = (size_t)cfg->M * cfg->N * 4;
+  if (overlaps(y, ybytes, xq, (size_t)cfg->M * cfg->K) || overlaps(y, ybytes, xs, (size_t)cfg->M * cfg->K / 32) ||
+      overlaps(y, ybytes, w, (size_t)cfg->N * cfg->K) || overlaps(y, ybytes, w_scale, (size_t)cfg->N * cfg->K / 32))
+    return MOE_ERR_ALIAS;
+  if (part_bytes && overlaps(y, ybytes, workspace, p.total)) return MOE_ERR_ALIAS;
+  return dense_gemm_checked(cfg, xq, xs, w, w_scale, y, part_bytes ? at<float>(workspace, p.part) : nullptr,
+                            (hipStream_t)stream);
+}
+
+int moe_dense_fp8_forward(const moe_dense_config* cfg, const void* x, const uint8_t* w, const uint8_t* w_scale,
+                          float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dense(cfg);
+  if (st) return st;
+  if (cfg->M == 0) return MOE_OK;
+  if (!x || !w || !w_scale || !y || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(w_scale) || !aligned16(y) || ((uintptr_t)workspace & 255))
+    return MOE_ERR_ALIGNMENT;
+  const DensePlan p = dense_plan(cfg);
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t ybytes = (size_t)cfg->M * cfg->N * 4;
+  const size_t xbytes = (size_t)cfg->M * cfg->K * (cfg->x_dtype == MOE_X_F32 ? 4 : 2);
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, w, (size_t)cfg->N * cfg->K) ||
+      overlaps(y, ybytes, w_scale, (size_t)cfg->N * cfg->K / 32) || overlaps(workspace, p.total, x, xbytes) ||
+      overlaps(workspace, p.total, y, ybytes))
+    return MOE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* xq = at<uint8_t>(workspace, p.xq);
+  uint8_t* xs = at<uint8_t>(workspace, p.xs);
+  MOE_TRY(moe_k_quant_mxfp8(cfg->x_dtype, x, cfg->M, cfg->K, xq, xs, s));
+  return dense_gemm_checked(cfg, xq, xs, w, w_scale, y, at<float>(workspace, p.part), s);
+}
+
+}  // extern "C"

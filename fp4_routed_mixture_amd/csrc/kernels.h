@@ -83,3 +83,15 @@ hipError_t moe_k_rmsnorm(const float* x, int T, int H, float* out, hipStream_t s
 hipError_t moe_k_residual(float* x, const float* y, int64_t n, hipStream_t st);
 hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, int H, int K, float* x,
                                        float* layer_out, float* xn, hipStream_t st);
+
+// gemm_dense.hip: block-scaled FP8 (MXFP8) dense projection y[M][N] =
+// x[M][K] w[N][K]^T; x codes/scales from moe_k_quant_mxfp8. M <= 32 runs the
+// small-batch kernel, which needs part (moe_k_dense_partial_bytes) when it
+// splits K over workgroups.
+int moe_k_dense_block_n();
+int moe_k_dense_split(int M, int N, int K);
+size_t moe_k_dense_partial_bytes(int M, int N, int K);
+hipError_t moe_k_quant_mxfp8(int in_dtype, const void* v, int rows, int K, uint8_t* codes, uint8_t* scales,
+                             hipStream_t st);
+hipError_t moe_k_dense_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, int M,
+                                int N, int K, float* y, float* part, hipStream_t st);

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define FP4MOE_ABI_VERSION 2
+#define FP4MOE_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum moe_status {
@@ -393,6 +393,65 @@ int moe_forward_stack_taps(const moe_config* cfg, int32_t L, float* x, const flo
                            const uint8_t* const* w13_scale, const uint8_t* const* w2, const uint8_t* const* w2_scale,
                            float* layer_out, const moe_taps* taps, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------------ dense FP8 --------
+ * Block-scaled FP8 dense projection y = x W^T, the format of the model's
+ * dense (non-expert) projections: FP8 dense projections (DeepSeek-V4-Flash on
+ * AMD gfx90a: Correctness Recovery and Inference Performance Engineering,
+ * abstract) with FP8 block quantization (DeepSeek V4 Flash on 8x AMD gfx1201,
+ * section What we set out to do). The pages fix neither the block shape nor
+ * the scale format; this library takes OCP MX FP8 (Microscaling v1.0):
+ *   - elements E4M3 (bias 7, no infinities, 0x7f / 0xff NaN, largest 448);
+ *   - one E8M0 scale byte (2^(byte - 127)) per 32 consecutive elements along
+ *     K, for every weight row and every activation row;
+ *   - activation quantization per block of 32: scale exponent
+ *     floor(log2 amax) - 8 biased by 127, clamped to [0, 254] (0 for an
+ *     all-zero block); values scaled by the exact power of two, rounded to
+ *     the nearest E4M3 value with ties to even, saturated at 448; the code's
+ *     sign is the value's sign bit;
+ *   - y[m][n] = sum over blocks b of 2^(sx[m][b] + sw[n][b] - 254) *
+ *     sum_{k in b} x[m][k] w[n][k], the products and their sums accumulated
+ *     in fp32 by the matrix cores (|error| <= K * 2^-23 * sum |terms|).
+ * Weights: w codes uint8 [N][K] (row-major), w_scale uint8 [N][K/32]; a
+ * code 0x7f / 0xff (NaN) propagates NaN. Same conventions as the calls above
+ * (device pointers owned by the caller, host-side checks, no allocation,
+ * no floating-point atomics: bit-identical results from run to run).
+ * Shape limits: 0 <= M <= 1<<20, K % 128 == 0 and 128 <= K <= 32768,
+ * N % 256 == 0 and 256 <= N <= 65536, M * K < 2^32. M = 0 does nothing. */
+typedef struct moe_dense_config {
+    int32_t M;       /* tokens (rows of x and y) */
+    int32_t N;       /* output features (rows of W) */
+    int32_t K;       /* input features */
+    int32_t x_dtype; /* enum moe_x_dtype: element type of x for moe_dense_fp8_forward */
+} moe_dense_config;
+
+/* Workspace of moe_dense_fp8_forward (the quantized activations and, for
+ * M <= 32, the partial sums of a K split) and of moe_dense_fp8_gemm (the
+ * partial sums only). Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE. */
+int moe_dense_fp8_workspace_size(const moe_dense_config* cfg, size_t* bytes);
+
+/* MXFP8 quantization of v [rows][K] (in_dtype MOE_X_F32 or MOE_X_BF16) into
+ * codes uint8 [rows][K] and scales uint8 [rows][K/32], the rule above.
+ * v and codes 16-byte aligned. Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED_SHAPE (K outside 32..65536 or not a multiple of 32),
+ * MOE_ERR_ALIGNMENT, MOE_ERR_HIP. */
+int moe_dense_fp8_quantize(int32_t rows, int32_t K, int32_t in_dtype, const void* v, uint8_t* codes,
+                           uint8_t* scales, void* stream);
+
+/* y fp32 [M][N] (overwritten) from quantized activations xq [M][K], xs
+ * [M][K/32] and the weights. workspace (256-byte aligned, at least
+ * moe_dense_fp8_workspace_size bytes) is read only when M <= 32 and may
+ * be NULL otherwise. All pointers 16-byte aligned; y must not overlap an
+ * input or the workspace. Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED_SHAPE, MOE_ERR_ALIGNMENT, MOE_ERR_ALIAS,
+ * MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP. */
+int moe_dense_fp8_gemm(const moe_dense_config* cfg, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
+                       const uint8_t* w_scale, float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The projection from activations: quantize x [M][K] (cfg->x_dtype) into
+ * the workspace, then the GEMM above into y fp32 [M][N]. Same errors. */
+int moe_dense_fp8_forward(const moe_dense_config* cfg, const void* x, const uint8_t* w, const uint8_t* w_scale,
+                          float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.moe_abi_version() == 2
+    assert B.moe_abi_version() == 3
     for s in range(7):
         assert B.moe_status_string(s) and B.moe_status_string(s) != "unknown status"
     assert B.moe_status_string(99) == "unknown status"
@@ -208,3 +208,58 @@ def test_stack_entry_point_errors(L):
     null_layer = C.cast((P * 1)(None), P)
     assert stack(c, ptrs=null_layer) == 1           # a layer without weights
     assert stack(c, ws=FAKE + (1 << 32)) == 4       # workspace overlaps the stream
+
+
+def dcfg(M=4604, N=4096, K=4096, x_dtype=1):
+    return B.moe_dense_config(M, N, K, x_dtype)
+
+
+def test_dense_config_struct_matches_header(L):
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct moe_dense_config \{(.*?)\} moe_dense_config;", src, re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert [n for n, _ in B.moe_dense_config._fields_] == fields == ["M", "N", "K", "x_dtype"]
+
+
+def test_dense_shape_checks_and_workspace(L):
+    n = C.c_size_t(0)
+    ws = lambda c: L.moe_dense_fp8_workspace_size(C.byref(c), C.byref(n))
+    assert ws(dcfg()) == 0
+    assert n.value >= 4604 * 4096 + 4604 * 128          # the quantized activations
+    assert ws(dcfg(M=32)) == 0 and n.value >= 32 * 4096 * 2 * 4  # plus the K-split partials
+    assert ws(dcfg(M=0)) == 0
+    for bad in (dcfg(K=100), dcfg(K=64), dcfg(K=65536), dcfg(N=128), dcfg(N=300), dcfg(M=-1), dcfg(M=(1 << 20) + 1),
+                dcfg(M=1 << 20, K=4096)):
+        assert ws(bad) == 2, bad
+    assert ws(dcfg(x_dtype=7)) == 1
+    assert L.moe_dense_fp8_workspace_size(None, C.byref(n)) == 1
+    assert L.moe_dense_fp8_workspace_size(C.byref(dcfg()), None) == 1
+
+
+def test_dense_entry_point_errors(L):
+    c = dcfg()
+    n = C.c_size_t(0)
+    assert L.moe_dense_fp8_workspace_size(C.byref(c), C.byref(n)) == 0
+    big = 1 << 32
+    x, w, s, y, work = FAKE, FAKE + big, FAKE + 2 * big, FAKE + 3 * big, FAKE + 4 * big
+    fwd = lambda cc=c, x=x, w=w, s=s, y=y, work=work, nb=n.value: L.moe_dense_fp8_forward(
+        C.byref(cc), x, w, s, y, work, nb, None)
+    assert fwd(x=None) == 1
+    assert fwd(work=None) == 1
+    assert fwd(x=x + 8) == 3
+    assert fwd(work=work + 16) == 3                       # workspace 256-byte aligned
+    assert fwd(nb=n.value - 1) == 5
+    assert fwd(y=x) == 4                                  # y over x
+    assert fwd(work=y) == 4                               # workspace over y
+    assert fwd(cc=dcfg(M=0), x=None, w=None, s=None, y=None, work=None) == 0
+    gemm = lambda cc=c, xq=x, xs=FAKE + 5 * big, y=y, work=None, nb=0: L.moe_dense_fp8_gemm(
+        C.byref(cc), xq, xs, w, s, y, work, nb, None)
+    assert gemm(xq=None) == 1
+    assert gemm(y=w) == 4                                 # y over the weights
+    assert gemm(xs=FAKE + 5 * big + 4) == 3
+    assert gemm(cc=dcfg(M=32)) == 5                       # the small-batch K split needs the workspace
+    q = lambda rows=4, K=256, dt=0, v=x, codes=y, sc=w: L.moe_dense_fp8_quantize(rows, K, dt, v, codes, sc, None)
+    assert q(K=48) == 2 and q(K=0) == 2 and q(rows=-1) == 2
+    assert q(dt=3) == 1 and q(v=None) == 1
+    assert q(codes=y + 8) == 3
+    assert q(rows=0, v=None, codes=None, sc=None) == 0
