@@ -30,7 +30,8 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_wo
            "moe_quantize",
            "moe_forward", "moe_forward_taps", "moe_forward_routed", "moe_rmsnorm", "moe_residual_add",
            "moe_stack_workspace_size", "moe_forward_stack", "moe_forward_stack_taps", "moe_forward_noalloc",
-           "moe_dense_fp8_workspace_size", "moe_dense_fp8_quantize", "moe_dense_fp8_gemm", "moe_dense_fp8_forward"]
+           "moe_dense_fp8_workspace_size", "moe_dense_fp8_quantize", "moe_dense_fp8_gemm", "moe_dense_fp8_forward",
+           "moe_dense_fp8_prepacked_size", "moe_dense_fp8_prepack", "moe_dense_fp8_unpack"]
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -52,7 +53,7 @@ class moe_config(C.Structure):
 
 
 class moe_dense_config(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("M", "N", "K", "x_dtype")]
+    _fields_ = [(n, C.c_int32) for n in ("M", "N", "K", "x_dtype", "weight_layout")]
 
     def __repr__(self):
         return "moe_dense_config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -106,6 +107,9 @@ def lib():
             "moe_dense_fp8_quantize": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
             "moe_dense_fp8_gemm": (C.c_int, [dcfgp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_dense_fp8_forward": (C.c_int, [dcfgp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_dense_fp8_prepacked_size": (C.c_int, [i32, i32, C.POINTER(sz), C.POINTER(sz)]),
+            "moe_dense_fp8_prepack": (C.c_int, [i32, i32, vp, vp, vp, vp, vp]),
+            "moe_dense_fp8_unpack": (C.c_int, [i32, i32, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -300,8 +304,24 @@ def moe_forward_stack_taps(cfg, x, layers, workspace, layer_taps, layer_out=None
 
 
 # ------------------------------------------------------------- dense FP8 --
-def make_dense_config(M, N, K, x_dtype=MOE_X_BF16) -> moe_dense_config:
-    return moe_dense_config(M, N, K, x_dtype)
+def make_dense_config(M, N, K, x_dtype=MOE_X_BF16, weight_layout=MOE_LAYOUT_CANONICAL) -> moe_dense_config:
+    return moe_dense_config(M, N, K, x_dtype, weight_layout)
+
+
+def moe_dense_fp8_prepacked_size(N, K):
+    cb, sb = C.c_size_t(0), C.c_size_t(0)
+    _check(lib().moe_dense_fp8_prepacked_size(N, K, C.byref(cb), C.byref(sb)), "moe_dense_fp8_prepacked_size")
+    return cb.value, sb.value
+
+
+def moe_dense_fp8_prepack(N, K, w, w_scale, packed_w, packed_scale, stream=None):
+    _check(lib().moe_dense_fp8_prepack(N, K, _p(w), _p(w_scale), _p(packed_w), _p(packed_scale), _s(stream)),
+           "moe_dense_fp8_prepack")
+
+
+def moe_dense_fp8_unpack(N, K, packed_w, packed_scale, w, w_scale, stream=None):
+    _check(lib().moe_dense_fp8_unpack(N, K, _p(packed_w), _p(packed_scale), _p(w), _p(w_scale), _s(stream)),
+           "moe_dense_fp8_unpack")
 
 
 def moe_dense_fp8_workspace_size(cfg) -> int:

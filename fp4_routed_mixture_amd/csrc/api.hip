@@ -562,6 +562,7 @@ namespace {
 int check_dense(const moe_dense_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->x_dtype != MOE_X_F32 && c->x_dtype != MOE_X_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->weight_layout != MOE_LAYOUT_CANONICAL && c->weight_layout != MOE_LAYOUT_PREPACKED) return MOE_ERR_INVALID_ARG;
   if (c->M < 0 || c->M > (1 << 20)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (c->K < 128 || c->K > 32768 || c->K % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
   const int bn = moe_k_dense_block_n();
@@ -571,22 +572,31 @@ int check_dense(const moe_dense_config* c) {
   return MOE_OK;
 }
 
+bool dense_small(const moe_dense_config* c) { return c->M <= 32; }
+
+// Workspace: the quantized token rows (M <= 32: one operand-packed 32-row
+// tile), then the K-split partial sums of the small-batch kernel.
 struct DensePlan {
   size_t xq, xs, part, total;
 };
 
 DensePlan dense_plan(const moe_dense_config* c) {
   DensePlan p;
+  const bool sm = dense_small(c);
   p.xq = 0;
-  p.xs = up256((size_t)c->M * c->K);
-  p.part = p.xs + up256((size_t)c->M * (c->K / 32));
+  p.xs = up256(sm ? (size_t)32 * c->K : (size_t)c->M * c->K);
+  p.part = p.xs + up256(sm ? moe_k_dense_packed_scale_bytes(32, c->K) : (size_t)c->M * (c->K / 32));
   p.total = p.part + up256(moe_k_dense_partial_bytes(c->M, c->N, c->K));
   return p;
 }
 
-int dense_gemm_checked(const moe_dense_config* c, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
-                       const uint8_t* w_scale, float* y, float* part, hipStream_t s) {
-  MOE_TRY(moe_k_dense_fp8_gemm(xq, xs, w, w_scale, c->M, c->N, c->K, y, part, s));
+size_t dense_w_scale_bytes(const moe_dense_config* c) {
+  return c->weight_layout == MOE_LAYOUT_PREPACKED ? moe_k_dense_packed_scale_bytes(c->N, c->K)
+                                                  : (size_t)c->N * (c->K / 32);
+}
+
+int dense_check_pack_shape(int32_t N, int32_t K) {
+  if (K < 128 || K > 32768 || K % 128 || N < 32 || N > 65536 || N % 32) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
 }
 
@@ -609,8 +619,42 @@ int moe_dense_fp8_quantize(int32_t rows, int32_t K, int32_t in_dtype, const void
   if (rows == 0) return MOE_OK;
   if (!v || !codes || !scales) return MOE_ERR_INVALID_ARG;
   if (!aligned16(v) || !aligned16(codes)) return MOE_ERR_ALIGNMENT;
-  MOE_TRY(moe_k_quant_mxfp8(in_dtype, v, rows, K, codes, scales, (hipStream_t)stream));
+  MOE_TRY(moe_k_quant_mxfp8(in_dtype, v, rows, K, 0, codes, scales, (hipStream_t)stream));
   return MOE_OK;
+}
+
+int moe_dense_fp8_prepacked_size(int32_t N, int32_t K, size_t* code_bytes, size_t* scale_bytes) {
+  const int st = dense_check_pack_shape(N, K);
+  if (st) return st;
+  if (!code_bytes || !scale_bytes) return MOE_ERR_INVALID_ARG;
+  *code_bytes = (size_t)N * K;
+  *scale_bytes = moe_k_dense_packed_scale_bytes(N, K);
+  return MOE_OK;
+}
+
+static int dense_pack_entry(int to_packed, int32_t N, int32_t K, const uint8_t* src_c, const uint8_t* src_s,
+                            uint8_t* dst_c, uint8_t* dst_s, void* stream) {
+  const int st = dense_check_pack_shape(N, K);
+  if (st) return st;
+  if (!src_c || !src_s || !dst_c || !dst_s) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src_c) || !aligned16(dst_c) || ((uintptr_t)(to_packed ? dst_s : src_s) & 3)) return MOE_ERR_ALIGNMENT;
+  const size_t cb = (size_t)N * K, ps = moe_k_dense_packed_scale_bytes(N, K), cs = (size_t)N * (K / 32);
+  const size_t sb_src = to_packed ? cs : ps, sb_dst = to_packed ? ps : cs;
+  if (overlaps(dst_c, cb, src_c, cb) || overlaps(dst_c, cb, src_s, sb_src) || overlaps(dst_s, sb_dst, src_c, cb) ||
+      overlaps(dst_s, sb_dst, src_s, sb_src) || overlaps(dst_c, cb, dst_s, sb_dst))
+    return MOE_ERR_ALIAS;
+  MOE_TRY(moe_k_dense_pack(to_packed, N, N, K, src_c, src_s, dst_c, dst_s, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_dense_fp8_prepack(int32_t N, int32_t K, const uint8_t* w, const uint8_t* w_scale, uint8_t* packed_w,
+                          uint8_t* packed_scale, void* stream) {
+  return dense_pack_entry(1, N, K, w, w_scale, packed_w, packed_scale, stream);
+}
+
+int moe_dense_fp8_unpack(int32_t N, int32_t K, const uint8_t* packed_w, const uint8_t* packed_scale, uint8_t* w,
+                         uint8_t* w_scale, void* stream) {
+  return dense_pack_entry(0, N, K, packed_w, packed_scale, w, w_scale, stream);
 }
 
 int moe_dense_fp8_gemm(const moe_dense_config* cfg, const uint8_t* xq, const uint8_t* xs, const uint8_t* w,
@@ -622,16 +666,25 @@ int moe_dense_fp8_gemm(const moe_dense_config* cfg, const uint8_t* xq, const uin
   if (!aligned16(xq) || !aligned16(xs) || !aligned16(w) || !aligned16(w_scale) || !aligned16(y))
     return MOE_ERR_ALIGNMENT;
   const DensePlan p = dense_plan(cfg);
-  const size_t part_bytes = moe_k_dense_partial_bytes(cfg->M, cfg->N, cfg->K);
-  if (part_bytes && (!workspace || workspace_bytes < p.total)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (part_bytes && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
-  const size_t ybytes = (size_t)cfg->M * cfg->N * 4;
+  const bool sm = dense_small(cfg);
+  if (sm && (!workspace || workspace_bytes < p.total)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (sm && ((uintptr_t)workspace & 255)) return MOE_ERR_ALIGNMENT;
+  const size_t ybytes = (size_t)cfg->M * cfg->N * 4, wsb = dense_w_scale_bytes(cfg);
   if (overlaps(y, ybytes, xq, (size_t)cfg->M * cfg->K) || overlaps(y, ybytes, xs, (size_t)cfg->M * cfg->K / 32) ||
-      overlaps(y, ybytes, w, (size_t)cfg->N * cfg->K) || overlaps(y, ybytes, w_scale, (size_t)cfg->N * cfg->K / 32))
+      overlaps(y, ybytes, w, (size_t)cfg->N * cfg->K) || overlaps(y, ybytes, w_scale, wsb))
     return MOE_ERR_ALIAS;
-  if (part_bytes && overlaps(y, ybytes, workspace, p.total)) return MOE_ERR_ALIAS;
-  return dense_gemm_checked(cfg, xq, xs, w, w_scale, y, part_bytes ? at<float>(workspace, p.part) : nullptr,
-                            (hipStream_t)stream);
+  if (sm && overlaps(y, ybytes, workspace, p.total)) return MOE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  const int pw = cfg->weight_layout == MOE_LAYOUT_PREPACKED;
+  if (sm) {  // the small-batch kernel reads the token tile operand-packed
+    uint8_t* tq = at<uint8_t>(workspace, p.xq);
+    uint8_t* ts = at<uint8_t>(workspace, p.xs);
+    MOE_TRY(moe_k_dense_pack(1, 32, cfg->M, cfg->K, xq, xs, tq, ts, s));
+    MOE_TRY(moe_k_dense_fp8_gemm(pw, tq, ts, w, w_scale, cfg->M, cfg->N, cfg->K, y, at<float>(workspace, p.part), s));
+  } else {
+    MOE_TRY(moe_k_dense_fp8_gemm(pw, xq, xs, w, w_scale, cfg->M, cfg->N, cfg->K, y, nullptr, s));
+  }
+  return MOE_OK;
 }
 
 int moe_dense_fp8_forward(const moe_dense_config* cfg, const void* x, const uint8_t* w, const uint8_t* w_scale,
@@ -644,17 +697,20 @@ int moe_dense_fp8_forward(const moe_dense_config* cfg, const void* x, const uint
     return MOE_ERR_ALIGNMENT;
   const DensePlan p = dense_plan(cfg);
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const size_t ybytes = (size_t)cfg->M * cfg->N * 4;
+  const size_t ybytes = (size_t)cfg->M * cfg->N * 4, wsb = dense_w_scale_bytes(cfg);
   const size_t xbytes = (size_t)cfg->M * cfg->K * (cfg->x_dtype == MOE_X_F32 ? 4 : 2);
   if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, w, (size_t)cfg->N * cfg->K) ||
-      overlaps(y, ybytes, w_scale, (size_t)cfg->N * cfg->K / 32) || overlaps(workspace, p.total, x, xbytes) ||
+      overlaps(y, ybytes, w_scale, wsb) || overlaps(workspace, p.total, x, xbytes) ||
       overlaps(workspace, p.total, y, ybytes))
     return MOE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   uint8_t* xq = at<uint8_t>(workspace, p.xq);
   uint8_t* xs = at<uint8_t>(workspace, p.xs);
-  MOE_TRY(moe_k_quant_mxfp8(cfg->x_dtype, x, cfg->M, cfg->K, xq, xs, s));
-  return dense_gemm_checked(cfg, xq, xs, w, w_scale, y, at<float>(workspace, p.part), s);
+  const bool sm = dense_small(cfg);
+  MOE_TRY(moe_k_quant_mxfp8(cfg->x_dtype, x, cfg->M, cfg->K, sm ? 1 : 0, xq, xs, s));
+  MOE_TRY(moe_k_dense_fp8_gemm(cfg->weight_layout == MOE_LAYOUT_PREPACKED, xq, xs, w, w_scale, cfg->M, cfg->N, cfg->K,
+                               y, sm ? at<float>(workspace, p.part) : nullptr, s));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -85,13 +85,19 @@ hipError_t moe_k_combine_residual_norm(const float* y, const float* w, int T, in
                                        float* layer_out, float* xn, hipStream_t st);
 
 // gemm_dense.hip: block-scaled FP8 (MXFP8) dense projection y[M][N] =
-// x[M][K] w[N][K]^T; x codes/scales from moe_k_quant_mxfp8. M <= 32 runs the
-// small-batch kernel, which needs part (moe_k_dense_partial_bytes) when it
-// splits K over workgroups.
+// x[M][K] w[N][K]^T. M <= 32 runs the small-batch kernel on an operand-packed
+// token tile (moe_k_quant_mxfp8 with packed, or moe_k_dense_pack; 32 rows)
+// and needs part (moe_k_dense_partial_bytes) when it splits K over
+// workgroups; larger M runs the wide kernel on canonical token rows. packed_w:
+// weights in the operand-packed layout of moe_k_dense_pack.
 int moe_k_dense_block_n();
 int moe_k_dense_split(int M, int N, int K);
+int moe_k_dense_wide_rows(int M, int N);
 size_t moe_k_dense_partial_bytes(int M, int N, int K);
-hipError_t moe_k_quant_mxfp8(int in_dtype, const void* v, int rows, int K, uint8_t* codes, uint8_t* scales,
-                             hipStream_t st);
-hipError_t moe_k_dense_fp8_gemm(const uint8_t* xq, const uint8_t* xs, const uint8_t* wq, const uint8_t* ws, int M,
-                                int N, int K, float* y, float* part, hipStream_t st);
+size_t moe_k_dense_packed_scale_bytes(int R, int K);
+hipError_t moe_k_quant_mxfp8(int in_dtype, const void* v, int rows, int K, int packed, uint8_t* codes,
+                             uint8_t* scales, hipStream_t st);
+hipError_t moe_k_dense_pack(int to_packed, int R, int rows_valid, int K, const uint8_t* src_c, const uint8_t* src_s,
+                            uint8_t* dst_c, uint8_t* dst_s, hipStream_t st);
+hipError_t moe_k_dense_fp8_gemm(int packed_w, const uint8_t* xq, const uint8_t* xs, const uint8_t* wq,
+                                const uint8_t* ws, int M, int N, int K, float* y, float* part, hipStream_t st);

@@ -412,23 +412,50 @@ int moe_forward_stack_taps(const moe_config* cfg, int32_t L, float* x, const flo
  *   - y[m][n] = sum over blocks b of 2^(sx[m][b] + sw[n][b] - 254) *
  *     sum_{k in b} x[m][k] w[n][k], the products and their sums accumulated
  *     in fp32 by the matrix cores (|error| <= K * 2^-23 * sum |terms|).
- * Weights: w codes uint8 [N][K] (row-major), w_scale uint8 [N][K/32]; a
- * code 0x7f / 0xff (NaN) propagates NaN. Same conventions as the calls above
+ * Weights, in the layout cfg->weight_layout names:
+ *   MOE_LAYOUT_CANONICAL: w codes uint8 [N][K] (row-major), w_scale uint8
+ *     [N][K/32];
+ *   MOE_LAYOUT_PREPACKED: the operand order of the matrix cores, made by
+ *     moe_dense_fp8_prepack once when the weights are loaded: codes
+ *     [N/32][K/64][2][64][16] (32-row tile, 64-K step, plane p, lane l, byte
+ *     b: row 32 tile + l % 32, k = 64 step + 32 p + 16 (l / 32) + b), so
+ *     every load is 1 KB contiguous; scales [N/32][ceil(K/256)][64] dwords,
+ *     byte j of lane l = the E8M0 byte of block 2 (4 g + j) + l / 32 of row
+ *     32 tile + l % 32 (127 past the last K-step).
+ * A code 0x7f / 0xff (NaN) propagates NaN. Same conventions as the calls above
  * (device pointers owned by the caller, host-side checks, no allocation,
  * no floating-point atomics: bit-identical results from run to run).
  * Shape limits: 0 <= M <= 1<<20, K % 128 == 0 and 128 <= K <= 32768,
  * N % 256 == 0 and 256 <= N <= 65536, M * K < 2^32. M = 0 does nothing. */
 typedef struct moe_dense_config {
-    int32_t M;       /* tokens (rows of x and y) */
-    int32_t N;       /* output features (rows of W) */
-    int32_t K;       /* input features */
-    int32_t x_dtype; /* enum moe_x_dtype: element type of x for moe_dense_fp8_forward */
+    int32_t M;             /* tokens (rows of x and y) */
+    int32_t N;             /* output features (rows of W) */
+    int32_t K;             /* input features */
+    int32_t x_dtype;       /* enum moe_x_dtype: element type of x for moe_dense_fp8_forward */
+    int32_t weight_layout; /* enum moe_weight_layout of w and w_scale */
 } moe_dense_config;
 
 /* Workspace of moe_dense_fp8_forward (the quantized activations and, for
- * M <= 32, the partial sums of a K split) and of moe_dense_fp8_gemm (the
- * partial sums only). Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE. */
+ * M <= 32, the partial sums of a K split) and of moe_dense_fp8_gemm (for
+ * M <= 32: the activations repacked into the operand order, and the partial
+ * sums). Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED_SHAPE. */
 int moe_dense_fp8_workspace_size(const moe_dense_config* cfg, size_t* bytes);
+
+/* Byte counts of the prepacked weight layout (codes: N * K; scales:
+ * N/32 * ceil(K/256) * 256). Shapes: N % 32 == 0, 32 <= N <= 65536, K % 128
+ * == 0, 128 <= K <= 32768. Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED_SHAPE. */
+int moe_dense_fp8_prepacked_size(int32_t N, int32_t K, size_t* code_bytes, size_t* scale_bytes);
+
+/* Canonical weights (w [N][K], w_scale [N][K/32]) to the prepacked layout
+ * above, and back (a bijection on the codes; the scale padding is dropped
+ * when unpacking). Code pointers 16-byte aligned, packed scales 4-byte
+ * aligned; the four buffers must not overlap. Errors: MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED_SHAPE, MOE_ERR_ALIGNMENT, MOE_ERR_ALIAS, MOE_ERR_HIP. */
+int moe_dense_fp8_prepack(int32_t N, int32_t K, const uint8_t* w, const uint8_t* w_scale, uint8_t* packed_w,
+                          uint8_t* packed_scale, void* stream);
+int moe_dense_fp8_unpack(int32_t N, int32_t K, const uint8_t* packed_w, const uint8_t* packed_scale, uint8_t* w,
+                         uint8_t* w_scale, void* stream);
 
 /* MXFP8 quantization of v [rows][K] (in_dtype MOE_X_F32 or MOE_X_BF16) into
  * codes uint8 [rows][K] and scales uint8 [rows][K/32], the rule above.
@@ -440,7 +467,7 @@ int moe_dense_fp8_quantize(int32_t rows, int32_t K, int32_t in_dtype, const void
 
 /* y fp32 [M][N] (overwritten) from quantized activations xq [M][K], xs
  * [M][K/32] and the weights. workspace (256-byte aligned, at least
- * moe_dense_fp8_workspace_size bytes) is read only when M <= 32 and may
+ * moe_dense_fp8_workspace_size bytes) is used only when M <= 32 and may
  * be NULL otherwise. All pointers 16-byte aligned; y must not overlap an
  * input or the workspace. Errors: MOE_ERR_INVALID_ARG,
  * MOE_ERR_UNSUPPORTED_SHAPE, MOE_ERR_ALIGNMENT, MOE_ERR_ALIAS,

@@ -210,15 +210,15 @@ def test_stack_entry_point_errors(L):
     assert stack(c, ws=FAKE + (1 << 32)) == 4       # workspace overlaps the stream
 
 
-def dcfg(M=4604, N=4096, K=4096, x_dtype=1):
-    return B.moe_dense_config(M, N, K, x_dtype)
+def dcfg(M=4604, N=4096, K=4096, x_dtype=1, weight_layout=0):
+    return B.moe_dense_config(M, N, K, x_dtype, weight_layout)
 
 
 def test_dense_config_struct_matches_header(L):
     src = open(HEADER).read()
     body = re.search(r"typedef struct moe_dense_config \{(.*?)\} moe_dense_config;", src, re.S).group(1)
     fields = re.findall(r"int32_t\s+(\w+);", body)
-    assert [n for n, _ in B.moe_dense_config._fields_] == fields == ["M", "N", "K", "x_dtype"]
+    assert [n for n, _ in B.moe_dense_config._fields_] == fields == ["M", "N", "K", "x_dtype", "weight_layout"]
 
 
 def test_dense_shape_checks_and_workspace(L):
@@ -226,12 +226,14 @@ def test_dense_shape_checks_and_workspace(L):
     ws = lambda c: L.moe_dense_fp8_workspace_size(C.byref(c), C.byref(n))
     assert ws(dcfg()) == 0
     assert n.value >= 4604 * 4096 + 4604 * 128          # the quantized activations
-    assert ws(dcfg(M=32)) == 0 and n.value >= 32 * 4096 * 2 * 4  # plus the K-split partials
+    assert ws(dcfg(M=32)) == 0 and n.value >= 32 * 4096          # one packed token tile
+    assert ws(dcfg(M=32, N=1536)) == 0 and n.value >= 32 * 1536 * 2 * 4  # plus the K-split partials
     assert ws(dcfg(M=0)) == 0
     for bad in (dcfg(K=100), dcfg(K=64), dcfg(K=65536), dcfg(N=128), dcfg(N=300), dcfg(M=-1), dcfg(M=(1 << 20) + 1),
                 dcfg(M=1 << 20, K=4096)):
         assert ws(bad) == 2, bad
     assert ws(dcfg(x_dtype=7)) == 1
+    assert ws(dcfg(weight_layout=2)) == 1
     assert L.moe_dense_fp8_workspace_size(None, C.byref(n)) == 1
     assert L.moe_dense_fp8_workspace_size(C.byref(dcfg()), None) == 1
 
@@ -263,3 +265,18 @@ def test_dense_entry_point_errors(L):
     assert q(dt=3) == 1 and q(v=None) == 1
     assert q(codes=y + 8) == 3
     assert q(rows=0, v=None, codes=None, sc=None) == 0
+    # prepacked weight layout: sizes, shapes, overlaps
+    cb, sb = C.c_size_t(0), C.c_size_t(0)
+    assert L.moe_dense_fp8_prepacked_size(4096, 4096, C.byref(cb), C.byref(sb)) == 0
+    assert (cb.value, sb.value) == (4096 * 4096, 4096 * 4096 // 32)
+    assert L.moe_dense_fp8_prepacked_size(64, 384, C.byref(cb), C.byref(sb)) == 0
+    assert (cb.value, sb.value) == (64 * 384, 2 * 2 * 256)          # two groups, the last one padded
+    assert L.moe_dense_fp8_prepacked_size(48, 4096, C.byref(cb), C.byref(sb)) == 2
+    assert L.moe_dense_fp8_prepacked_size(64, 4096, None, C.byref(sb)) == 1
+    pk = lambda src=x, srcs=FAKE + 5 * big, dst=w, dsts=s, N=256, K=256: L.moe_dense_fp8_prepack(
+        N, K, src, srcs, dst, dsts, None)
+    assert pk(N=100) == 2 and pk(K=200) == 2
+    assert pk(src=None) == 1
+    assert pk(dst=w + 4) == 3 and pk(dsts=s + 2) == 3
+    assert pk(dst=x + 128) == 4                                    # codes over codes
+    assert L.moe_dense_fp8_unpack(256, 256, x, FAKE + 5 * big + 2, w, s, None) == 3  # packed scales 4-byte aligned

@@ -214,21 +214,27 @@ def test_gemm_special_scales():
 
 @pytest.mark.parametrize("name", ["dense_t4604", "dense_t16384", "dense_t4604_n1536"])
 def test_forward_full_size_sampled(name):
-    """The full-size projection as timed (quantize on the device, then the
-    GEMM), checked on sampled token rows that cover the first and the last
-    (ragged) 64-row tile and rows spread over the batch."""
+    """The full-size projection as timed (prepacked weights; quantize on the
+    device, then the GEMM), checked on sampled token rows: the first rows,
+    both sides of the 128-row wave tile and the 256-row workgroup tile
+    boundaries, the last (ragged) rows and rows spread over the batch."""
     w = S.DENSE_WORKLOADS[name]
     print(f"[dense forward] {name} M={w.M} N={w.N} K={w.K}", flush=True)
     wq_h, ws_h = S.dense_weights(w)
+    cb, sb = B.moe_dense_fp8_prepacked_size(w.N, w.K)
+    pw = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_prepack(w.N, w.K, to_dev(wq_h), to_dev(ws_h), pw, ps)
     x = S.dense_activations(w)
-    cfg = B.make_dense_config(w.M, w.N, w.K, w.x_dtype)
+    cfg = B.make_dense_config(w.M, w.N, w.K, w.x_dtype, B.MOE_LAYOUT_PREPACKED)
     work = torch.empty(B.moe_dense_fp8_workspace_size(cfg), dtype=torch.uint8, device="cuda")
     y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-    B.moe_dense_fp8_forward(cfg, to_dev(x), to_dev(wq_h), to_dev(ws_h), y, work)
+    B.moe_dense_fp8_forward(cfg, to_dev(x), pw, ps, y, work)
     torch.cuda.synchronize()
-    last = (w.M - 1) // 64 * 64
-    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(62, 66), np.arange(last, w.M),
-                                     np.random.default_rng(5).choice(w.M, 24, replace=False)]))
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(126, 130), np.arange(254, 258),
+                                     np.arange(w.M - 6, w.M),
+                                     np.random.default_rng(5).choice(w.M, 20, replace=False)]))
+    rows = rows[rows < w.M]
     xq, xs = oracle.quant_mxfp8(x_f32(x[rows]))
     check_bound(y[torch.from_numpy(rows).cuda()].cpu().numpy(), *oracle_with_bound(xq, xs, wq_h, ws_h), w.K, name)
 
@@ -270,3 +276,71 @@ def test_zero_rows_and_errors():
     B.moe_dense_fp8_forward(cfg, x, w, s, y, work)
     torch.cuda.synchronize()
     assert torch.all(y == 0)
+
+
+def host_pack(wq, ws):
+    """The prepacked layout as the header defines it, built on the host."""
+    N, K = wq.shape
+    KT, G = K // 64, (K // 64 + 3) // 4
+    pc = np.empty((N // 32, KT, 2, 64, 16), np.uint8)
+    ps = np.full((N // 32, G, 64, 4), 127, np.uint8)
+    for l in range(64):
+        c, h = l % 32, l // 32
+        for p in range(2):
+            for kt in range(KT):
+                k0 = 64 * kt + 32 * p + 16 * h
+                pc[:, kt, p, l, :] = wq[c::32, k0:k0 + 16]
+        for g in range(G):
+            for j in range(4):
+                if 4 * g + j < KT:
+                    ps[:, g, l, j] = ws[c::32, 2 * (4 * g + j) + h]
+    return pc.reshape(-1), ps.reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(64, 384), (512, 4096)])
+def test_prepack_layout_and_roundtrip(N, K):
+    w = S.DenseWorkload("pack", 1, K, N, S.X_F32, 40)
+    wq, ws = S.dense_weights(w)
+    cb, sb = B.moe_dense_fp8_prepacked_size(N, K)
+    pw = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_prepack(N, K, to_dev(wq), to_dev(ws), pw, ps)
+    uq = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    us = torch.empty((N, K // 32), dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_unpack(N, K, pw, ps, uq, us)
+    torch.cuda.synchronize()
+    hc, hs = host_pack(wq, ws)
+    assert np.array_equal(pw.cpu().numpy(), hc)
+    assert np.array_equal(ps.cpu().numpy(), hs)
+    assert np.array_equal(uq.cpu().numpy(), wq) and np.array_equal(us.cpu().numpy(), ws)
+
+
+@pytest.mark.parametrize("name", ["dense_tiny", "dense_t32", "dense_m1_k4096", "dense_m17_k1152", "dense_m100_k384",
+                                  "dense_m64_k640", "dense_m200_k2048"])
+def test_prepacked_equals_canonical(name):
+    """The GEMMs on prepacked weights give the canonical-layout result bit for
+    bit (the kernels differ only in their weight address maps), through both
+    entry points."""
+    w = dense_case(name)
+    print(f"[dense prepacked] {name} M={w.M} N={w.N} K={w.K}", flush=True)
+    wq_h, ws_h = S.dense_weights(w)
+    wq, ws = to_dev(wq_h), to_dev(ws_h)
+    cb, sb = B.moe_dense_fp8_prepacked_size(w.N, w.K)
+    pw = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_prepack(w.N, w.K, wq, ws, pw, ps)
+    x = to_dev(S.dense_activations(w))
+    xq_h, xs_h = oracle.quant_mxfp8(x_f32(S.dense_activations(w)))
+    outs = []
+    for layout, (a, b) in ((B.MOE_LAYOUT_CANONICAL, (wq, ws)), (B.MOE_LAYOUT_PREPACKED, (pw, ps))):
+        cfg = B.make_dense_config(w.M, w.N, w.K, w.x_dtype, layout)
+        work = torch.empty(max(B.moe_dense_fp8_workspace_size(cfg), 1), dtype=torch.uint8, device="cuda")
+        y1 = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        y2 = torch.empty_like(y1)
+        B.moe_dense_fp8_forward(cfg, x, a, b, y1, work)
+        B.moe_dense_fp8_gemm(cfg, to_dev(xq_h), to_dev(xs_h), a, b, y2, work)
+        torch.cuda.synchronize()
+        outs.append((y1.cpu().numpy(), y2.cpu().numpy()))
+    for i in range(2):
+        assert np.array_equal(outs[0][i].view(np.uint32), outs[1][i].view(np.uint32)), name
+    check_bound(outs[1][1], *oracle_with_bound(xq_h, xs_h, wq_h, ws_h), w.K, name)
