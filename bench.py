@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -361,6 +362,54 @@ def run_ep_rank(name: str, ranks: int, steps: int, warmup: int, torch, B, S, SD,
             "hbm_gbs": used * (b13 + b2) / (ms / 1e3) / 1e9}
 
 
+def run_dense(name: str, steps: int, warmup: int, torch, B, S, sleep_ms: float = 20.0) -> dict:
+    """The block-scaled FP8 dense projection on prepacked weights: a step is
+    one moe_dense_fp8_forward (quantize x, then the GEMM); the GEMM alone is
+    timed by events around moe_dense_fp8_gemm on pre-quantized rows (for
+    M > 32 that call is the wide kernel alone)."""
+    w = S.DENSE_WORKLOADS[name]
+    wq_h, ws_h = S.dense_weights(w)
+    wq, ws = torch.from_numpy(wq_h).cuda(), torch.from_numpy(ws_h).cuda()
+    cb, sb = B.moe_dense_fp8_prepacked_size(w.N, w.K)
+    pw = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_prepack(w.N, w.K, wq, ws, pw, ps)
+    del wq, ws
+    x = torch.from_numpy(S.dense_activations(w)).cuda()
+    cfg = B.make_dense_config(w.M, w.N, w.K, w.x_dtype, B.MOE_LAYOUT_PREPACKED)
+    work = torch.empty(B.moe_dense_fp8_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    xq = torch.empty((w.M, w.K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((w.M, w.K // 32), dtype=torch.uint8, device="cuda")
+    B.moe_dense_fp8_quantize(w.M, w.K, w.x_dtype, x, xq, xs)
+    for _ in range(warmup):
+        B.moe_dense_fp8_forward(cfg, x, pw, ps, y, work)
+    torch.cuda.synchronize()
+    total_ms, per, _ = timed_steps(lambda i: B.moe_dense_fp8_forward(cfg, x, pw, ps, y, work), steps, torch, sleep_ms)
+    _, per_gemm, _ = timed_steps(lambda i: B.moe_dense_fp8_gemm(cfg, xq, xs, pw, ps, y, work), steps, torch, sleep_ms)
+    fwd_ms, gemm_ms = total_ms / steps, float(np.mean(per_gemm))
+    flops = 2.0 * w.M * w.N * w.K
+    wbytes = w.N * w.K * (1 + 1 / 32)
+    xbytes = w.M * w.K * (2 if w.x_dtype == S.X_BF16 else 4)
+    gemm_bytes = wbytes + w.M * w.K * (1 + 1 / 32) + w.M * w.N * 4
+    return {"workload": name, "M": w.M, "N": w.N, "K": w.K, "steps": steps,
+            "ms_per_step": fwd_ms, "step_ms": step_stats(per), "tokens_per_s": w.M / (fwd_ms / 1e3),
+            "fwd_tflops": flops / (fwd_ms / 1e3) / 1e12,
+            "fwd_hbm_gbs": (wbytes + xbytes + w.M * w.N * 4) / (fwd_ms / 1e3) / 1e9,
+            "gemm_ms": gemm_ms, "gemm_step_ms": step_stats(per_gemm), "gemm_alg_flops": flops,
+            "gemm_alg_bytes": gemm_bytes, "gemm_tflops": flops / (gemm_ms / 1e3) / 1e12,
+            "gemm_gbs": gemm_bytes / (gemm_ms / 1e3) / 1e9}
+
+
+def dense_summary(v: dict) -> dict:
+    return {"M": v["M"], "N": v["N"], "K": v["K"], "tokens_per_s": round(v["tokens_per_s"], 1),
+            "ms_per_step": round(v["ms_per_step"], 5), "step_ms": v["step_ms"],
+            "fwd_fp8_tflops": round(v["fwd_tflops"], 1), "fwd_fp8_frac": round(v["fwd_tflops"] / FP8_PEAK_TFLOPS, 4),
+            "fwd_hbm_gbs": round(v["fwd_hbm_gbs"], 1), "fwd_hbm_frac": round(v["fwd_hbm_gbs"] / HBM_PEAK_GBS, 4),
+            "gemm_us": round(v["gemm_ms"] * 1e3, 2), "gemm_fp8_tflops": round(v["gemm_tflops"], 1),
+            "gemm_fp8_frac": round(v["gemm_tflops"] / FP8_PEAK_TFLOPS, 4), "gemm_gbs": round(v["gemm_gbs"], 1)}
+
+
 def cpu_baseline(name: str, budget_s: float, S, oracle) -> dict:
     """The oracle, untuned, on the host cores, on a bounded sample of the
     same workload: for the layer stack, consecutive layers of the stack on
@@ -503,12 +552,15 @@ def main():
                     help="headline workload: the 43-layer decode stack (default) or a single-layer workload")
     ap.add_argument("--rot", type=int, default=8, help="distinct layers cycled through (single-layer workloads)")
     ap.add_argument("--legs", default="prefill_t16384_zipf,decode_t4,decode_t64_zipf,prefill_t4604_zipf,"
-                                      "decode_t4_tp4,prefill_t4604_zipf_tp4,prefill_t4604_zipf_ep8",
+                                      "decode_t4_tp4,prefill_t4604_zipf_tp4,prefill_t4604_zipf_ep8,"
+                                      "dense_t16384,dense_t4604,dense_t32",
                     help="comma-separated legs to run after the headline workload ('' for none)")
     ap.add_argument("--no-legs", action="store_true", help="run the headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only run the FP4 MFMA rate / shader clock probe and print its JSON")
+    ap.add_argument("--dense", default="",
+                    help="only run the named dense FP8 projection workload (--steps, --warmup) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -534,6 +586,9 @@ def main():
     from fp4_routed_mixture_amd import synth_device as SD
     if args.mfma_probe:
         print(json.dumps(mfma_probe(torch, SD)))
+        return
+    if args.dense:
+        print(json.dumps(dense_summary(run_dense(args.dense, args.steps, args.warmup, torch, B, S))))
         return
     B.lib()
     ev = HipEvents()
@@ -570,6 +625,16 @@ def main():
         ep = run_ep_rank("prefill_t4604_zipf", 8, 10, 2, torch, B, S, SD)
         print(f"# prefill_t4604_zipf_ep8: {ep['ms_per_step'] * 1e3:.1f} us/step, {ep['pairs']} pairs "
               f"({100 * ep['pair_share']:.1f}% of all), {ep['fp4_tflops']:.0f} TF/s", file=sys.stderr, flush=True)
+    dense = {}
+    for name, steps in (("dense_t16384", 20), ("dense_t4604", 20), ("dense_t32", 50)):
+        if name not in want:
+            continue
+        torch.cuda.empty_cache()
+        d = run_dense(name, steps, 3, torch, B, S)
+        dense[name] = d
+        print(f"# {name}: forward {d['ms_per_step'] * 1e3:.1f} us ({d['fwd_tflops']:.0f} TF/s, "
+              f"{d['fwd_hbm_gbs']:.0f} GB/s), GEMM {d['gemm_ms'] * 1e3:.1f} us ({d['gemm_tflops']:.0f} TF/s)",
+              file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
     stream_gbs = streaming_read_gbs(torch, SD)
 
@@ -612,6 +677,18 @@ def main():
                    "layer_fp4_frac": round(pf["layer_fp4_tflops"] / FP4_PEAK_TFLOPS, 4),
                    "layer_tokens_per_s": round(pf["tokens_per_s"], 1)}
 
+    # the dense FP8 projection's GEMM at 16,384 tokens against the FP8 peak
+    roof_dense = None
+    if "dense_t16384" in dense:
+        d = dense["dense_t16384"]
+        k = "dense_fp8_wide_kernel<true,4>"
+        prof = profiled(k, "dense_t16384")
+        roof_dense = {"bound": "mfma", "kernel": k, "workload": "dense_t16384", "achieved": round(d["gemm_tflops"], 1),
+                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(d["gemm_tflops"] / FP8_PEAK_TFLOPS, 4),
+                      "traffic": prof["bytes_per_launch"] if prof else None,
+                      "alg_flops_per_launch": d["gemm_alg_flops"], "avg_launch_us": round(d["gemm_ms"] * 1e3, 2),
+                      "launches_timed": d["steps"]}
+
     import oracle
     cpu = cpu_baseline(args.workload, args.cpu_seconds, S, oracle)
 
@@ -635,11 +712,14 @@ def main():
                    "routing": "zipf1.1" if w.zipf else "uniform"},
         "roofline": roof,
         "roofline_prefill": roof_pf,
+        "roofline_dense": roof_dense,
         "cpu_baseline": cpu,
         "graph": {"ms_per_step": round(head["graph_ms_per_step"], 5),
                   "tokens_per_s": round(head["graph_tokens_per_s"], 1)},
         "legs": {k: leg_summary(v) for k, v in legs.items()},
     }
+    for k, v in dense.items():
+        line["legs"][k] = dense_summary(v)
     if not stack_head:
         line["stage_us_diagnostic"] = {k: round(v * 1e3, 2) for k, v in head["stage_ms"].items()}
     else:
