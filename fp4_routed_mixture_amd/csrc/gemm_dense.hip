@@ -145,9 +145,8 @@ __global__ __launch_bounds__(256, 1) void dense_fp8_wide_kernel(const uint8_t* _
     for (int u = 0; u < WNU; ++u) sx[u] = *reinterpret_cast<const uint32_t*>(xs + xs_off[u] + 4 * g);
 #pragma unroll
     for (int t = 0; t < WFT; ++t) {
-      if constexpr (PW) {  // the lane's bytes of the K-step pair, in bytes 0 and 1
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(ws_row + t * ws_tile + (size_t)(g >> 1) * 256);
-        sw[t] = d >> (16 * (g & 1));
+      if constexpr (PW) {  // the dword of four K-steps; the pair's half is picked at use
+        sw[t] = *reinterpret_cast<const uint32_t*>(ws_row + t * ws_tile + (size_t)(g >> 1) * 256);
       } else {
         sw[t] = *reinterpret_cast<const uint32_t*>(ws_row + t * ws_tile + 4 * g);
       }
@@ -158,13 +157,15 @@ __global__ __launch_bounds__(256, 1) void dense_fp8_wide_kernel(const uint8_t* _
     for (int u = 0; u < WNU; ++u)
       bx[set][u] = *reinterpret_cast<const v8i*>(&lds[slot * WSLOT + ((ti * WNU + u) * 2 + k) * 2048 + lane * 32]);
   };
-  auto kstep = [&](auto k_c, int kt_next) {
+  // (scales are picked here, not where they are loaded: an operation on a
+  // just-loaded value would wait for that load within the group)
+  auto kstep = [&](auto k_c, int kt_next, uint32_t wsh) {
     constexpr int k = decltype(k_c)::value;
     uint32_t sa[WNU], sb[WFT];
 #pragma unroll
     for (int u = 0; u < WNU; ++u) sa[u] = pick2(sxc[u], psel);
 #pragma unroll
-    for (int t = 0; t < WFT; ++t) sb[t] = PW ? swc[t] : pick2(swc[t], psel);
+    for (int t = 0; t < WFT; ++t) sb[t] = PW ? swc[t] >> wsh : pick2(swc[t], psel);
 #pragma unroll
     for (int u = 0; u < WNU; ++u)
 #pragma unroll
@@ -192,10 +193,11 @@ __global__ __launch_bounds__(256, 1) void dense_fp8_wide_kernel(const uint8_t* _
     __builtin_amdgcn_sched_barrier(0);
     bread(1, cur, 1);
     __builtin_amdgcn_sched_barrier(0);
-    kstep(DIC<0>(), 2 * g + 2);
+    const uint32_t wsh = 16u * (uint32_t)(g & 1);  // packed weights: this group's half of the scale dword
+    kstep(DIC<0>(), 2 * g + 2, wsh);
     bread(0, nxt, 0);
     __builtin_amdgcn_sched_barrier(0);
-    kstep(DIC<1>(), 2 * g + 3);
+    kstep(DIC<1>(), 2 * g + 3, wsh);
     xstore(fut);
     __syncthreads();
 #pragma unroll
