@@ -56,8 +56,13 @@ struct Group {
   uint32_t sa0, sa1;
 };
 
+// Prepacked tiles are read once, nontemporally. A canonical row is read in
+// 32-byte pieces, four K-steps to a 128-byte line: plain loads keep the line
+// for the next pieces (nontemporal ones measured slower there).
+template <bool CANON>
 __device__ __forceinline__ v4i ld_weights(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  if constexpr (CANON) return *reinterpret_cast<const v4i*>(p);
+  else return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
 }
 
 // The scale dword of a canonical row for K-step group g (K-steps 4g..4g+3):
@@ -97,8 +102,8 @@ __device__ __forceinline__ void load_group(Group<S>& G, const uint8_t* aptr, con
     G.a1[u] = (v4i){0, 0, 0, 0};
     G.b[u] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
     if (kt < KT) {
-      G.a0[u] = ld_weights(aptr + (size_t)kt * a_step);
-      if (S == 2) G.a1[u] = ld_weights(aptr + (size_t)kt * a_step + a1_off);
+      G.a0[u] = ld_weights<CANON>(aptr + (size_t)kt * a_step);
+      if (S == 2) G.a1[u] = ld_weights<CANON>(aptr + (size_t)kt * a_step + a1_off);
       if (valid) {
         const v4i lo = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64);
         const v4i hi = *reinterpret_cast<const v4i*>(bptr + (size_t)kt * 64 + 32);

@@ -89,6 +89,12 @@ enum moe_status {
 enum moe_x_dtype { MOE_X_F32 = 0, MOE_X_BF16 = 1 };       /* activation element type */
 enum moe_act_mode { MOE_ACT_INT8 = 0, MOE_ACT_MXFP4 = 1 }; /* activation quantization */
 enum moe_weight { MOE_W13 = 0, MOE_W2 = 1 };               /* which expert matrix */
+/* Both layouts give identical results. The canonical rows are read by the
+ * kernels 32 rows x 32 bytes a load; the prepacked tiles 1 KB contiguous a
+ * load. On MI355X canonical weights ran the 4-token decode layer in about
+ * 110 us against 72 us prepacked, the 64-token one in 572 against 298 us and
+ * the 4,604-token prefill layer in 1.65 against 1.21 ms: prepack once when
+ * the weights are loaded (moe_prepack). */
 enum moe_weight_layout {
     MOE_LAYOUT_CANONICAL = 0, /* the interchange layout described under "weights" below */
     MOE_LAYOUT_PREPACKED = 1  /* the MFMA operand layout that moe_prepack writes (faster) */
