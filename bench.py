@@ -503,29 +503,31 @@ def streaming_read_gbs(torch, SD, gib: int = 8, reps: int = 5) -> float:
 
 
 def mfma_probe(torch, SD, iters: int = 40000) -> dict:
-    """Scaled FP4 MFMA issue rate on random operands, with one and two waves
-    per SIMD: TFLOP/s from events and the shader clock measured in-kernel
-    (s_memtime cycles over the 100 MHz s_memrealtime)."""
+    """Scaled MFMA issue rate on random FP4 and FP8 operands, with one and two
+    waves per SIMD: TFLOP/s from events and the shader clock measured
+    in-kernel (s_memtime cycles over the 100 MHz s_memrealtime)."""
     res = {}
-    for per_simd in (1, 2):
-        blocks = 256 * per_simd  # 4 waves a workgroup: one per SIMD
-        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-        clocks = torch.empty(blocks * 8, dtype=torch.int64, device="cuda")
-        SD.mfma_probe(blocks, 100, out, clocks)
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        SD.mfma_probe(blocks, iters, out, clocks)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1)
-        flops = blocks * 4 * iters * 8 * 131072.0
-        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
-        mhz = c[:, 0] / (c[:, 1] / 100.0)
-        res[f"waves_per_simd_{per_simd}"] = {
-            "tflops": round(flops / (ms / 1e3) / 1e12, 1), "ms": round(ms, 3),
-            "shader_mhz_median": round(float(np.median(mhz)), 1),
-            "cycles_per_mfma_per_simd": round(float(np.median(c[:, 0])) / (iters * 8 * per_simd), 2)}
+    for fmt, fp8, n in (("fp4", False, iters), ("fp8", True, iters // 2)):
+        for per_simd in (1, 2):
+            blocks = 256 * per_simd  # 4 waves a workgroup: one per SIMD
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            clocks = torch.empty(blocks * 8, dtype=torch.int64, device="cuda")
+            SD.mfma_probe(blocks, 100, out, clocks, fp8)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            SD.mfma_probe(blocks, n, out, clocks, fp8)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            flops = blocks * 4 * n * 8 * 131072.0
+            c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+            mhz = c[:, 0] / (c[:, 1] / 100.0)
+            key = f"waves_per_simd_{per_simd}" if fmt == "fp4" else f"fp8_waves_per_simd_{per_simd}"
+            res[key] = {
+                "tflops": round(flops / (ms / 1e3) / 1e12, 1), "ms": round(ms, 3),
+                "shader_mhz_median": round(float(np.median(mhz)), 1),
+                "cycles_per_mfma_per_simd": round(float(np.median(c[:, 0])) / (n * 8 * per_simd), 2)}
     return res
 
 

@@ -9,8 +9,9 @@
 // oracle's over the whole input range.
 // The same benchmark-support library holds two probes: a plain streaming read
 // (the practical HBM read ceiling that the weight-streaming kernels are set
-// beside) and a scaled-FP4 MFMA issue loop on random operands with the shader
-// clock read in-kernel (the matrix rate the chip sustains under that load).
+// beside) and a scaled-MFMA issue loop on random FP4 or FP8 operands with the
+// shader clock read in-kernel (the matrix rate the chip sustains under that
+// load).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,11 +69,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Eight independent accumulators per wave, each fed one
-// V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4, 131,072 FLOP) per iteration
-// on operands drawn from a per-lane xorshift stream (random E2M1 codes, scale
-// 1); every wave records its shader-clock and 100 MHz constant-clock deltas.
-__global__ __launch_bounds__(256) void mfma_fp4_probe_kernel(int iters, uint32_t seed, float* __restrict__ out,
-                                                             uint64_t* __restrict__ clocks) {
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 (131,072 FLOP) per iteration on operands
+// drawn from a per-lane xorshift stream, scale 1: FP8 = false, FP4 x FP4
+// (random E2M1 codes in the first four dwords); FP8 = true, E4M3 x E4M3
+// (codes with the top two bits cleared: exponent fields 0..7, all finite).
+// Every wave records its shader-clock and 100 MHz constant-clock deltas.
+template <bool FP8>
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint32_t seed, float* __restrict__ out,
+                                                         uint64_t* __restrict__ clocks) {
   uint32_t st = seed ^ (blockIdx.x * 256u + threadIdx.x) * 0x9E3779B9u;
   auto next = [&]() {
     st ^= st << 13;
@@ -85,8 +89,8 @@ __global__ __launch_bounds__(256) void mfma_fp4_probe_kernel(int iters, uint32_t
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      a[u][k] = k < 4 ? next() : 0;
-      b[u][k] = k < 4 ? next() : 0;
+      a[u][k] = FP8 ? (next() & 0x3f3f3f3f) : (k < 4 ? next() : 0);
+      b[u][k] = FP8 ? (next() & 0x3f3f3f3f) : (k < 4 ? next() : 0);
     }
   f32x16 acc[8];
 #pragma unroll
@@ -95,8 +99,8 @@ __global__ __launch_bounds__(256) void mfma_fp4_probe_kernel(int iters, uint32_t
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 1], b[(j >> 1) & 1], acc[j], 4, 4, 0, 127, 0,
-                                                                127);
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 1], b[(j >> 1) & 1], acc[j], FP8 ? 0 : 4,
+                                                               FP8 ? 0 : 4, 0, 127, 0, 127);
   }
   const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float sum = 0.f;
@@ -131,13 +135,23 @@ int synth_exp_sigmoid(const float* z, int n, float* e, float* s, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// The FP4 MFMA probe: blocks workgroups of 4 waves, iters iterations of 8
-// MFMAs per wave. out: blocks * 256 floats; clocks: blocks * 4 * 2 uint64
-// (shader-clock and 100 MHz-clock deltas of each wave).
-int synth_mfma_probe(int blocks, int iters, void* out, void* clocks, void* stream) {
+// The MFMA rate probe: blocks workgroups of 4 waves, iters iterations of 8
+// MFMAs per wave, FP4 (fp8 == 0) or FP8 operands. out: blocks * 256 floats;
+// clocks: blocks * 4 * 2 uint64 (shader-clock and 100 MHz-clock deltas of
+// each wave).
+int synth_mfma_probe_fmt(int blocks, int iters, int fp8, void* out, void* clocks, void* stream) {
   if (blocks < 1 || iters < 1 || !out || !clocks) return 1;
-  mfma_fp4_probe_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out, (uint64_t*)clocks);
+  if (fp8)
+    mfma_probe_kernel<true><<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out,
+                                                                    (uint64_t*)clocks);
+  else
+    mfma_probe_kernel<false><<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out,
+                                                                     (uint64_t*)clocks);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int synth_mfma_probe(int blocks, int iters, void* out, void* clocks, void* stream) {
+  return synth_mfma_probe_fmt(blocks, iters, 0, out, clocks, stream);
 }
 
 // Streaming read of nbytes (multiple of 16, 16-byte aligned) at src with

@@ -36,6 +36,8 @@ def slib():
         L.synth_exp_sigmoid.argtypes = [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         L.synth_mfma_probe.restype = C.c_int
         L.synth_mfma_probe.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.synth_mfma_probe_fmt.restype = C.c_int
+        L.synth_mfma_probe_fmt.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         L.synth_stream_read.restype = C.c_int
         L.synth_stream_read.argtypes = [C.c_void_p, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
         _slib = L
@@ -123,11 +125,11 @@ def stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor) -> None:
         raise RuntimeError(f"synth_stream_read failed ({rc})")
 
 
-def mfma_probe(blocks: int, iters: int, out: torch.Tensor, clocks: torch.Tensor) -> None:
-    """Enqueue the FP4 MFMA rate probe (a benchmark ceiling, not part of the
-    layer): out holds blocks * 256 floats, clocks blocks * 8 int64."""
-    rc = slib().synth_mfma_probe(blocks, iters, out.data_ptr(), clocks.data_ptr(),
-                                 torch.cuda.current_stream().cuda_stream)
+def mfma_probe(blocks: int, iters: int, out: torch.Tensor, clocks: torch.Tensor, fp8: bool = False) -> None:
+    """Enqueue the FP4 (or FP8) MFMA rate probe (a benchmark ceiling, not part
+    of the layer): out holds blocks * 256 floats, clocks blocks * 8 int64."""
+    rc = slib().synth_mfma_probe_fmt(blocks, iters, 1 if fp8 else 0, out.data_ptr(), clocks.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_mfma_probe failed ({rc})")
 
