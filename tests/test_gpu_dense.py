@@ -111,9 +111,15 @@ def special_rows(K=256):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("case", ["dense_tiny", "dense_t32", "special_f32", "special_bf16", "dense_t4604"])
+@pytest.mark.parametrize("case", ["dense_tiny", "dense_t32", "special_f32", "special_bf16", "dense_t4604", "kmax_bf16"])
 def test_quantize_bitexact(case):
-    if case.startswith("special"):
+    if case == "kmax_bf16":
+        # the quantizer's largest K (65536) on rows of mixed magnitude
+        rng = np.random.default_rng(45)
+        x = (rng.standard_normal((5, 65536)) * np.exp2(rng.integers(-30, 31, (5, 2048))).repeat(32, axis=1))
+        x = S.f32_to_bf16_bits(x.astype(np.float32))
+        in_dtype = B.MOE_X_BF16
+    elif case.startswith("special"):
         x = special_rows()
         in_dtype = B.MOE_X_F32
         if case == "special_bf16":
@@ -151,6 +157,14 @@ def dense_case(name):
         "dense_m1_k4096": S.DenseWorkload("dense_m1_k4096", 1, 4096, 1536, S.X_BF16, 34),
         "dense_m17_k1152": S.DenseWorkload("dense_m17_k1152", 17, 1152, 8192, S.X_F32, 35),
         "dense_m200_k2048": S.DenseWorkload("dense_m200_k2048", 200, 2048, 2304, S.X_BF16, 36),
+        # the largest K the ABI accepts, on both kernels: 128-row wide tiles
+        # over 512 K-steps, and the small-batch kernel split 8 ways along K
+        # (16 chunks of four K-steps per part)
+        "dense_m40_kmax": S.DenseWorkload("dense_m40_kmax", 40, 32768, 256, S.X_BF16, 38),
+        "dense_m3_kmax": S.DenseWorkload("dense_m3_kmax", 3, 32768, 512, S.X_F32, 39),
+        # the largest N: 256 workgroups of 256 features, 2048 small-batch tiles
+        "dense_m40_nmax": S.DenseWorkload("dense_m40_nmax", 40, 128, 65536, S.X_BF16, 41),
+        "dense_m3_nmax": S.DenseWorkload("dense_m3_nmax", 3, 256, 65536, S.X_F32, 42),
     }
     return extra[name]
 
@@ -165,7 +179,8 @@ def run_gemm(w, xq, xs, wq, ws):
 
 
 @pytest.mark.parametrize("name", ["dense_tiny", "dense_t32", "dense_m100_k384", "dense_m33_k128", "dense_m64_k640",
-                                  "dense_m1_k4096", "dense_m17_k1152", "dense_m200_k2048"])
+                                  "dense_m1_k4096", "dense_m17_k1152", "dense_m200_k2048", "dense_m40_kmax",
+                                  "dense_m3_kmax", "dense_m40_nmax", "dense_m3_nmax"])
 def test_gemm_parity(name):
     w = dense_case(name)
     print(f"[dense gemm] {name} M={w.M} N={w.N} K={w.K}", flush=True)
@@ -237,6 +252,40 @@ def test_forward_full_size_sampled(name):
     rows = rows[rows < w.M]
     xq, xs = oracle.quant_mxfp8(x_f32(x[rows]))
     check_bound(y[torch.from_numpy(rows).cuda()].cpu().numpy(), *oracle_with_bound(xq, xs, wq_h, ws_h), w.K, name)
+
+
+def test_forward_max_rows_sampled():
+    """2^20 token rows of K = 3968, so that the quantized rows fill 4.16e9 of
+    the 2^32 bytes the token offsets may span: sampled rows at the start, on
+    both sides of the 2^31-byte point and at the end must match the oracle.
+    The activations come from torch's seeded device generator (a bf16 normal
+    with a per-row power-of-two spread); only the sampled rows come to the
+    host."""
+    M, K, N = 1 << 20, 3968, 256
+    print(f"[dense forward max rows] M={M} N={N} K={K}", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(43)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    step = 1 << 16
+    for i in range(0, M, step):
+        spread = torch.exp2(torch.randint(-6, 7, (step, 1), generator=gen, device="cuda").float())
+        x[i:i + step] = (torch.randn((step, K), generator=gen, device="cuda") * spread).to(torch.bfloat16)
+    w = S.DenseWorkload("dense_max_rows", 1, K, N, S.X_BF16, 44)
+    wq_h, ws_h = S.dense_weights(w)
+    cfg = B.make_dense_config(M, N, K, B.MOE_X_BF16)
+    work = torch.empty(B.moe_dense_fp8_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    B.moe_dense_fp8_forward(cfg, x, to_dev(wq_h), to_dev(ws_h), y, work)
+    torch.cuda.synchronize()
+    mid = (1 << 31) // K
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(mid - 2, mid + 3), np.arange(M - 4, M),
+                                     np.random.default_rng(6).choice(M, 16, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    xr = x[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    xq, xs = oracle.quant_mxfp8(x_f32(xr))
+    check_bound(y[idx].cpu().numpy(), *oracle_with_bound(xq, xs, wq_h, ws_h), K, "max rows")
+    del x, work, y
+    torch.cuda.empty_cache()
 
 
 def test_forward_equals_quantize_then_gemm_and_repeats():
