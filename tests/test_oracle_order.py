@@ -17,31 +17,10 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+from exact_fp import add32, fma32, fma32_vec, round_f32
 from fp4_routed_mixture_amd import synth as S
 
 P24 = 2.0 ** 24
-
-
-# ------------------------------------------------------------ fp32 rounding
-def round_f32(q: Fraction) -> np.float32:
-    """The fp32 value nearest to the rational q, ties to even (one rounding:
-    the candidates around q are compared exactly, no double rounding)."""
-    f = np.float32(float(q))
-    cands = [f, np.nextafter(f, np.float32(-np.inf)), np.nextafter(f, np.float32(np.inf))]
-    cands = [c for c in cands if np.isfinite(c)]
-    best = min(abs(Fraction(float(c)) - q) for c in cands)
-    near = [c for c in cands if abs(Fraction(float(c)) - q) == best]
-    if len(near) == 1:
-        return near[0]
-    return [c for c in near if (int(np.array(c).view(np.uint32)) & 1) == 0][0]
-
-
-def fma32(a, b, c) -> np.float32:
-    return round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
-
-
-def add32(a, b) -> np.float32:
-    return round_f32(Fraction(float(a)) + Fraction(float(b)))
 
 
 def test_round_f32_helper():
@@ -49,6 +28,19 @@ def test_round_f32_helper():
     assert round_f32(Fraction(2 ** 24 + 3)) == P24 + 4      # tie to even (upward)
     assert round_f32(Fraction(1, 3)) == np.float32(1 / 3)
     assert fma32(1 + 2.0 ** -12, 1 + 2.0 ** -12, -(1 + 2.0 ** -11)) == 2.0 ** -24
+    # the vectorized fma against the rational one, including a case that
+    # double rounding gets wrong: (4097 * 2^-30) * (16773121 * 2^-30) + 1 is
+    # 1 + 2^-24 + 2^-60 (4097 * 16773121 = 2^36 + 1), which rounds to the
+    # midpoint 1 + 2^-24 in float64 and then to 1 in fp32; the fma gives
+    # 1 + 2^-23
+    a, b = np.float32(4097 * 2.0 ** -30), np.float32(16773121 * 2.0 ** -30)
+    assert fma32_vec(a, b, np.float32(1)) == np.float32(1 + 2.0 ** -23) == fma32(a, b, 1.0)
+    assert fma32_vec(-a, b, np.float32(-1)) == np.float32(-(1 + 2.0 ** -23))
+    rng = np.random.default_rng(3)
+    x, y, z = ((rng.standard_normal(3000) * np.exp2(rng.integers(-30, 30, 3000))).astype(np.float32) for _ in range(3))
+    z[:1000] = -(x[:1000].astype(np.float64) * y[:1000]).astype(np.float32)  # heavy cancellation
+    v = fma32_vec(x, y, z)
+    assert all(v[i] == fma32(x[i], y[i], z[i]) for i in range(3000))
 
 
 # ------------------------------------------------------- router logits (R6)
