@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from fp4_routed_mixture_amd import binding as B
 from fp4_routed_mixture_amd import synth as S
 from fp4_routed_mixture_amd import synth_device as SD
 from gpu_util import assert_close_rms, oracle_layer, require_gpu, run_forward
@@ -72,3 +73,43 @@ def test_large_experts(name, T, H, I, E, k):
     assert int((g["aq"] != o["aq"]).sum()) == 0
     assert_close_rms(g["out"], o["out"])
     del layer
+
+
+def test_max_tokens_sampled():
+    """The most tokens the 32-bit activation offsets of the prefill GEMMs
+    allow: 2^20 tokens of H = 7936, whose MXFP4 codes fill 4.16e9 of the 2^32
+    bytes, k = 1 over 4 experts (about 2^18 rows, thousands of sort tiles, per
+    expert). x comes from torch's seeded device generator. Routing and the
+    output are compared with the oracle on sampled tokens: the first ones,
+    both sides of the 2^31-byte point of the quantized x, the last ones and
+    random ones (a token's output depends on its own row only)."""
+    T, H, I, E, k = 1 << 20, 7936, 256, 4, 1
+    w = S.Workload("max_tokens", T, H, I, E, k, S.X_BF16, S.ACT_MXFP4, False, 45)
+    print(f"[limits] {S.describe(w)}", flush=True)
+    layer = SD.load_layer(w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(46)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    step = 1 << 16
+    for i in range(0, T, step):
+        x[i:i + step] = torch.randn((step, H), generator=gen, device="cuda").to(torch.bfloat16)
+    cfg = SD.config(w, T)
+    ws = SD.workspace(cfg)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_forward(cfg, x, layer["router_w"], layer["bias"], layer["w13"], layer["w13s"], layer["w2"], layer["w2s"],
+                  out, ids, wts, ws)
+    torch.cuda.synchronize()
+    mid = (1 << 31) // (H // 2)
+    rows = np.unique(np.concatenate([np.arange(0, 3), np.arange(mid - 2, mid + 3), np.arange(T - 3, T),
+                                     np.random.default_rng(7).choice(T, 24, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    xr = x[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+    o = oracle_layer(w, xr)
+    assert np.array_equal(ids[idx].cpu().numpy(), o["ids"])
+    assert np.array_equal(wts[idx].cpu().numpy().view(np.uint32), o["w"].view(np.uint32))
+    err, rms = assert_close_rms(out[idx].cpu().numpy(), o["out"])
+    print(f"  {len(rows)} sampled tokens: max|err| {err:.3g} (rms {rms:.3g})", flush=True)
+    del x, out, ws, layer
+    torch.cuda.empty_cache()
