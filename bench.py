@@ -503,27 +503,28 @@ def streaming_read_gbs(torch, SD, gib: int = 8, reps: int = 5) -> float:
 
 
 def mfma_probe(torch, SD, iters: int = 40000) -> dict:
-    """Scaled MFMA issue rate on random FP4 and FP8 operands, with one and two
-    waves per SIMD: TFLOP/s from events and the shader clock measured
-    in-kernel (s_memtime cycles over the 100 MHz s_memrealtime)."""
+    """MFMA issue rate on random operands -- the scaled 32x32x64 on FP4 and
+    FP8, the 32x32x2 on fp32 (the router's) -- with one and two waves per
+    SIMD: TFLOP/s from events and the shader clock measured in-kernel
+    (s_memtime cycles over the 100 MHz s_memrealtime)."""
     res = {}
-    for fmt, fp8, n in (("fp4", False, iters), ("fp8", True, iters // 2)):
+    for fmt, n, flop in (("fp4", iters, 131072.0), ("fp8", iters // 2, 131072.0), ("fp32", iters // 4, 4096.0)):
         for per_simd in (1, 2):
             blocks = 256 * per_simd  # 4 waves a workgroup: one per SIMD
             out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
             clocks = torch.empty(blocks * 8, dtype=torch.int64, device="cuda")
-            SD.mfma_probe(blocks, 100, out, clocks, fp8)
+            SD.mfma_probe(blocks, 100, out, clocks, fmt)
             torch.cuda.synchronize()
             t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t0.record()
-            SD.mfma_probe(blocks, n, out, clocks, fp8)
+            SD.mfma_probe(blocks, n, out, clocks, fmt)
             t1.record()
             torch.cuda.synchronize()
             ms = t0.elapsed_time(t1)
-            flops = blocks * 4 * n * 8 * 131072.0
+            flops = blocks * 4 * n * 8 * flop
             c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
             mhz = c[:, 0] / (c[:, 1] / 100.0)
-            key = f"waves_per_simd_{per_simd}" if fmt == "fp4" else f"fp8_waves_per_simd_{per_simd}"
+            key = f"waves_per_simd_{per_simd}" if fmt == "fp4" else f"{fmt}_waves_per_simd_{per_simd}"
             res[key] = {
                 "tflops": round(flops / (ms / 1e3) / 1e12, 1), "ms": round(ms, 3),
                 "shader_mhz_median": round(float(np.median(mhz)), 1),

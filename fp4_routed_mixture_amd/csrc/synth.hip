@@ -116,6 +116,46 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, uint32_t see
   }
 }
 
+// The same probe on the fp32 matrix cores (32x32x2 f32, 4,096 FLOP an
+// instruction) with random fp32 operands: magnitudes in [1, 2) with random
+// mantissas and signs, as the router's products are.
+__global__ __launch_bounds__(256) void mfma_probe_f32_kernel(int iters, uint32_t seed, float* __restrict__ out,
+                                                             uint64_t* __restrict__ clocks) {
+  uint32_t st = seed ^ (blockIdx.x * 256u + threadIdx.x) * 0x9E3779B9u;
+  auto next = [&]() {
+    st ^= st << 13;
+    st ^= st >> 17;
+    st ^= st << 5;
+    return st;
+  };
+  float a[2], b[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    a[u] = __uint_as_float(0x3f800000u | (next() & 0x807fffffu));
+    b[u] = __uint_as_float(0x3f800000u | (next() & 0x807fffffu));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = (f32x16){};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j & 1], b[(j >> 1) & 1], acc[j], 0, 0, 0);
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[j][v];
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+  if ((threadIdx.x & 63) == 0) {
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    clocks[2 * w] = t1 - t0;
+    clocks[2 * w + 1] = r1 - r0;
+  }
+}
+
 __global__ void exp_sigmoid_kernel(const float* __restrict__ z, int n, float* __restrict__ e, float* __restrict__ s) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -139,9 +179,13 @@ int synth_exp_sigmoid(const float* z, int n, float* e, float* s, void* stream) {
 // MFMAs per wave, FP4 (fp8 == 0) or FP8 operands. out: blocks * 256 floats;
 // clocks: blocks * 4 * 2 uint64 (shader-clock and 100 MHz-clock deltas of
 // each wave).
-int synth_mfma_probe_fmt(int blocks, int iters, int fp8, void* out, void* clocks, void* stream) {
-  if (blocks < 1 || iters < 1 || !out || !clocks) return 1;
-  if (fp8)
+// fmt: 0 FP4 x FP4, 1 FP8 x FP8 (scaled 32x32x64), 2 fp32 (32x32x2).
+int synth_mfma_probe_fmt(int blocks, int iters, int fmt, void* out, void* clocks, void* stream) {
+  if (blocks < 1 || iters < 1 || !out || !clocks || fmt < 0 || fmt > 2) return 1;
+  if (fmt == 2)
+    mfma_probe_f32_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out,
+                                                                   (uint64_t*)clocks);
+  else if (fmt == 1)
     mfma_probe_kernel<true><<<blocks, 256, 0, (hipStream_t)stream>>>(iters, 0x2545F491u, (float*)out,
                                                                     (uint64_t*)clocks);
   else

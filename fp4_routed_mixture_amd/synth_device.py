@@ -125,10 +125,12 @@ def stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor) -> None:
         raise RuntimeError(f"synth_stream_read failed ({rc})")
 
 
-def mfma_probe(blocks: int, iters: int, out: torch.Tensor, clocks: torch.Tensor, fp8: bool = False) -> None:
-    """Enqueue the FP4 (or FP8) MFMA rate probe (a benchmark ceiling, not part
-    of the layer): out holds blocks * 256 floats, clocks blocks * 8 int64."""
-    rc = slib().synth_mfma_probe_fmt(blocks, iters, 1 if fp8 else 0, out.data_ptr(), clocks.data_ptr(),
+def mfma_probe(blocks: int, iters: int, out: torch.Tensor, clocks: torch.Tensor, fmt: str = "fp4") -> None:
+    """Enqueue the MFMA rate probe (a benchmark ceiling, not part of the
+    layer) on fmt "fp4" or "fp8" (scaled 32x32x64) or "fp32" (32x32x2)
+    operands: out holds blocks * 256 floats, clocks blocks * 8 int64."""
+    code = {"fp4": 0, "fp8": 1, "fp32": 2}[fmt]
+    rc = slib().synth_mfma_probe_fmt(blocks, iters, code, out.data_ptr(), clocks.data_ptr(),
                                      torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_mfma_probe failed ({rc})")
