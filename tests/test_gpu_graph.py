@@ -123,3 +123,49 @@ def test_layer_graph_replays(name, T, H, I, E, k, act):
     rms = float(np.sqrt(np.mean(o["out"].astype(np.float64) ** 2)))
     assert float(np.abs(got - o["out"]).max()) <= TOL * rms
     del L, ws
+
+
+@pytest.mark.parametrize("M,N,K,layout", [
+    (17, 1536, 4096, B.MOE_LAYOUT_PREPACKED),   # small-batch kernel, K split over workgroups + reduce
+    (200, 2304, 2048, B.MOE_LAYOUT_CANONICAL),  # wide kernel, 128-row tiles
+])
+def test_dense_graph_replays(M, N, K, layout):
+    """The FP8 dense projection (quantizer + GEMM, and the K-split reduction
+    of small batches) captured and replayed with other inputs in place: every
+    replay equals the eager call on the same input bit for bit."""
+    w = S.DenseWorkload("graph_dense", M, K, N, S.X_BF16, 47)
+    print(f"[graph] dense M={M} N={N} K={K} layout={layout}", flush=True)
+    wq_h, ws_h = S.dense_weights(w)
+    wq, wsc = torch.from_numpy(wq_h).cuda(), torch.from_numpy(ws_h).cuda()
+    if layout == B.MOE_LAYOUT_PREPACKED:
+        cb, sb = B.moe_dense_fp8_prepacked_size(N, K)
+        pq = torch.empty(cb, dtype=torch.uint8, device="cuda")
+        ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+        B.moe_dense_fp8_prepack(N, K, wq, wsc, pq, ps)
+        wq, wsc = pq, ps
+    cfg = B.make_dense_config(M, N, K, S.X_BF16, layout)
+    work = torch.empty(B.moe_dense_fp8_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    inputs = [torch.from_numpy(S.dense_activations(S.DenseWorkload("graph_dense", M, K, N, S.X_BF16, 48 + i))
+                               .view(np.int16)).cuda() for i in range(3)]
+    x = torch.empty_like(inputs[0])
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def call():
+        B.moe_dense_fp8_forward(cfg, x, wq, wsc, y, work)
+
+    refs = []
+    for xi in inputs:
+        x.copy_(xi)
+        call()
+        torch.cuda.synchronize()
+        refs.append(y.clone())
+    g = _capture(call)
+    for rep in range(6):
+        i = rep % 3
+        x.copy_(inputs[i])
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), refs[i].view(torch.int32)), f"replay {rep} differs"
+        call()  # eager work between replays, on the same workspace
+        torch.cuda.synchronize()
