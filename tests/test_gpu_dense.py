@@ -393,3 +393,38 @@ def test_prepacked_equals_canonical(name):
     for i in range(2):
         assert np.array_equal(outs[0][i].view(np.uint32), outs[1][i].view(np.uint32)), name
     check_bound(outs[1][1], *oracle_with_bound(xq_h, xs_h, wq_h, ws_h), w.K, name)
+
+
+def _sweep(n=12, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((int(rng.choice([1, 2, 7, 31, 32, 33, 64, 129, 200])), 256 * int(rng.integers(1, 9)),
+                    128 * int(rng.integers(1, 17)), int(rng.integers(0, 2)), int(rng.integers(0, 2)), 60 + i))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,layout,xd,seed", _sweep())
+def test_forward_shape_sweep(M, N, K, layout, xd, seed):
+    """A seeded sweep of shapes through moe_dense_fp8_forward, either weight
+    layout and either activation type: the quantized x must match the oracle
+    (checked through the GEMM input it implies) and the output lie within the
+    derived bound of the oracle's exact block sums."""
+    w = S.DenseWorkload("dense_sweep", M, K, N, xd, seed)
+    print(f"[dense sweep] M={M} N={N} K={K} layout={layout} x={xd}", flush=True)
+    wq_h, ws_h = S.dense_weights(w)
+    wq, wsc = to_dev(wq_h), to_dev(ws_h)
+    if layout == B.MOE_LAYOUT_PREPACKED:
+        cb, sb = B.moe_dense_fp8_prepacked_size(N, K)
+        pq = torch.empty(cb, dtype=torch.uint8, device="cuda")
+        ps = torch.empty(sb, dtype=torch.uint8, device="cuda")
+        B.moe_dense_fp8_prepack(N, K, wq, wsc, pq, ps)
+        wq, wsc = pq, ps
+    x = S.dense_activations(w)
+    cfg = B.make_dense_config(M, N, K, xd, layout)
+    work = torch.empty(max(B.moe_dense_fp8_workspace_size(cfg), 1), dtype=torch.uint8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    B.moe_dense_fp8_forward(cfg, to_dev(x), wq, wsc, y, work)
+    torch.cuda.synchronize()
+    xq, xs = oracle.quant_mxfp8(x_f32(x))
+    check_bound(y.cpu().numpy(), *oracle_with_bound(xq, xs, wq_h, ws_h), K, f"sweep M{M} N{N} K{K}")
