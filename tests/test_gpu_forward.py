@@ -192,3 +192,37 @@ def test_forward_every_top_k(k):
     o = oracle_layer(w, S.activations(w))
     assert np.array_equal(g["ids"], o["ids"])
     assert np.array_equal(g["out"], o["out"])
+
+
+def test_int8_beyond_the_exact_range_is_within_tolerance():
+    """The output contract is the tolerance; int8 bit-exactness holds only
+    while every partial block sum is exact in fp32. Here the weight scale
+    bytes spread over 118..140, so block terms range from 2^-10 to 2^12 times
+    their integer sums and the partial sums need more than 24 bits; the
+    decode kernels' K split over four waves then adds them in another order
+    than the oracle's ascending blocks and may round differently. Routing
+    still matches bit for bit and the output stays within 2e-3 x RMS."""
+    T, H, I, E, k = 8, 2048, 512, 8, 2
+    rng = np.random.default_rng(61)
+    experts = [(rng.integers(0, 256, (2 * I, H // 2)).astype(np.uint8),
+                rng.integers(118, 141, (2 * I, H // 32)).astype(np.uint8),
+                rng.integers(0, 256, (H, I // 2)).astype(np.uint8),
+                rng.integers(118, 141, (H, I // 32)).astype(np.uint8)) for _ in range(E)]
+    wr = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    x = (100 * rng.standard_normal((T, H))).astype(np.float32)
+    print(f"[forward] wide-scale int8 T={T} H={H} I={I} E={E} k={k}", flush=True)
+    dev = [torch.from_numpy(np.stack([ex[i] for ex in experts])).cuda() for i in range(4)]
+    cfg = B.make_config(T, H, I, E, k, S.X_F32, S.ACT_INT8, B.MOE_LAYOUT_CANONICAL)
+    ws = SD.workspace(cfg)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_forward(cfg, torch.from_numpy(x).cuda(), torch.from_numpy(wr).cuda(), None, *dev, out, ids, wts, ws)
+    torch.cuda.synchronize()
+    o = oracle.moe_layer(x, wr, None, experts, k, 0)
+    assert np.array_equal(ids.cpu().numpy(), o["ids"])
+    assert np.array_equal(wts.cpu().numpy().view(np.uint32), o["w"].view(np.uint32))
+    g = out.cpu().numpy()
+    err, rms = assert_close_rms(g, o["out"])
+    print(f"  {int((g != o['out']).sum())} of {g.size} outputs differ from the oracle; max|err| {err:.3g} "
+          f"(rms {rms:.3g})", flush=True)
