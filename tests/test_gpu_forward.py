@@ -226,3 +226,47 @@ def test_int8_beyond_the_exact_range_is_within_tolerance():
     err, rms = assert_close_rms(g, o["out"])
     print(f"  {int((g != o['out']).sum())} of {g.size} outputs differ from the oracle; max|err| {err:.3g} "
           f"(rms {rms:.3g})", flush=True)
+
+
+def test_mxfp4_requant_of_tiny_activations():
+    """The gate/up epilogue's MXFP4 requantization where the hardware
+    conversion does not reach: blocks of `a` whose scale exponent falls
+    below 2 take the software encoder, including subnormal values and blocks
+    of zeros. Handmade weights make every gate value -6 sum(xq) and every up
+    value 2^-11 sum(xq), so token t's `a` is one value repeated over I; x
+    rows scaled over [0.040, 0.062] put g between about -61 and -95: some
+    tokens' blocks convert in hardware, some in software (sigma(g) itself
+    subnormal near -88.7) and some are zero (sigma(g) = 0 past the exp's
+    overflow). The requantized codes and scales must match the oracle byte
+    for byte."""
+    T, H, I, E, k = 64, 256, 128, 1, 1
+    rng = np.random.default_rng(62)
+    w13 = np.empty((2 * I, H // 2), np.uint8)
+    w13[:I] = 0xFF      # E2M1 code 15 = -6 in both nibbles
+    w13[I:] = 0x22      # code 2 = +1
+    w13s = np.empty((2 * I, H // 32), np.uint8)
+    w13s[:I] = 127
+    w13s[I:] = 116
+    w2 = rng.integers(0, 256, (H, I // 2)).astype(np.uint8)
+    w2s = rng.integers(121, 126, (H, I // 32)).astype(np.uint8)
+    experts = [(w13, w13s, w2, w2s)]
+    wr = np.full((E, H), 0.01, np.float32)
+    c = np.linspace(0.040, 0.062, T).astype(np.float32)
+    x = (c[:, None] * rng.uniform(0.5, 1.5, (T, H))).astype(np.float32)
+    print(f"[forward] tiny-activation requant T={T} H={H} I={I}", flush=True)
+    dev = [torch.from_numpy(a[None]).cuda() for a in (w13, w13s, w2, w2s)]
+    cfg = B.make_config(T, H, I, E, k, S.X_F32, S.ACT_MXFP4, B.MOE_LAYOUT_CANONICAL)
+    ws = SD.workspace(cfg)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    taps = {"aq": torch.empty((T, I // 2), dtype=torch.uint8, device="cuda"),
+            "as": torch.empty((T, I // 32), dtype=torch.uint8, device="cuda")}
+    B.moe_forward_taps(cfg, torch.from_numpy(x).cuda(), torch.from_numpy(wr).cuda(), None, *dev, out, None, None,
+                       taps, ws)
+    torch.cuda.synchronize()
+    o = oracle.moe_layer(x, wr, None, experts, k, 1, intermediates=True)
+    g_as = taps["as"].cpu().numpy()
+    assert np.array_equal(taps["aq"].cpu().numpy(), o["aq"]), "requantized codes differ"
+    assert np.array_equal(g_as, o["as"]), "requantized scales differ"
+    # the case covers both encoders: scale bytes >= 2 (hardware), < 2 (software), and all-zero blocks
+    assert (g_as >= 2).any() and (g_as < 2).any() and (o["aq"] == 0).all(axis=1).any()
+    assert_close_rms(out.cpu().numpy(), o["out"])
