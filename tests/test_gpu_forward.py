@@ -228,7 +228,8 @@ def test_int8_beyond_the_exact_range_is_within_tolerance():
           f"(rms {rms:.3g})", flush=True)
 
 
-def test_mxfp4_requant_of_tiny_activations():
+@pytest.mark.parametrize("act", [S.ACT_MXFP4, S.ACT_INT8])
+def test_requant_of_tiny_activations(act):
     """The gate/up epilogue's MXFP4 requantization where the hardware
     conversion does not reach: blocks of `a` whose scale exponent falls
     below 2 take the software encoder, including subnormal values and blocks
@@ -238,7 +239,8 @@ def test_mxfp4_requant_of_tiny_activations():
     tokens' blocks convert in hardware, some in software (sigma(g) itself
     subnormal near -88.7) and some are zero (sigma(g) = 0 past the exp's
     overflow). The requantized codes and scales must match the oracle byte
-    for byte."""
+    for byte; in int8 mode (row scales amax / 127 of subnormal amax, and
+    zero rows with scale 0) the output bit for bit as well."""
     T, H, I, E, k = 64, 256, 128, 1, 1
     rng = np.random.default_rng(62)
     w13 = np.empty((2 * I, H // 2), np.uint8)
@@ -255,18 +257,25 @@ def test_mxfp4_requant_of_tiny_activations():
     x = (c[:, None] * rng.uniform(0.5, 1.5, (T, H))).astype(np.float32)
     print(f"[forward] tiny-activation requant T={T} H={H} I={I}", flush=True)
     dev = [torch.from_numpy(a[None]).cuda() for a in (w13, w13s, w2, w2s)]
-    cfg = B.make_config(T, H, I, E, k, S.X_F32, S.ACT_MXFP4, B.MOE_LAYOUT_CANONICAL)
+    mx = act == S.ACT_MXFP4
+    cfg = B.make_config(T, H, I, E, k, S.X_F32, act, B.MOE_LAYOUT_CANONICAL)
     ws = SD.workspace(cfg)
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    taps = {"aq": torch.empty((T, I // 2), dtype=torch.uint8, device="cuda"),
-            "as": torch.empty((T, I // 32), dtype=torch.uint8, device="cuda")}
+    taps = {"aq": torch.empty((T, I // 2) if mx else (T, I), dtype=torch.uint8 if mx else torch.int8, device="cuda"),
+            "as": torch.empty((T, I // 32) if mx else (T,), dtype=torch.uint8 if mx else torch.float32,
+                              device="cuda")}
     B.moe_forward_taps(cfg, torch.from_numpy(x).cuda(), torch.from_numpy(wr).cuda(), None, *dev, out, None, None,
                        taps, ws)
     torch.cuda.synchronize()
-    o = oracle.moe_layer(x, wr, None, experts, k, 1, intermediates=True)
+    o = oracle.moe_layer(x, wr, None, experts, k, act, intermediates=True)
     g_as = taps["as"].cpu().numpy()
     assert np.array_equal(taps["aq"].cpu().numpy(), o["aq"]), "requantized codes differ"
-    assert np.array_equal(g_as, o["as"]), "requantized scales differ"
-    # the case covers both encoders: scale bytes >= 2 (hardware), < 2 (software), and all-zero blocks
-    assert (g_as >= 2).any() and (g_as < 2).any() and (o["aq"] == 0).all(axis=1).any()
-    assert_close_rms(out.cpu().numpy(), o["out"])
+    assert np.array_equal(g_as.view(np.uint8), np.ascontiguousarray(o["as"]).view(np.uint8)), "scales differ"
+    assert (o["aq"] == 0).all(axis=1).any()  # zero rows
+    if mx:
+        # both encoders: scale bytes >= 2 (hardware), < 2 (software)
+        assert (g_as >= 2).any() and (g_as < 2).any()
+        assert_close_rms(out.cpu().numpy(), o["out"])
+    else:
+        assert ((g_as > 0) & (g_as < 2.0 ** -126)).any()  # subnormal row scales
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), o["out"].view(np.uint32))
