@@ -76,6 +76,24 @@ def per_expert_bytes(w):
     return w13, w2
 
 
+def layer_accounting(w, T: int, d_layer: float, d_gate_up: float, x_bf16: bool, int8: bool) -> dict:
+    """Algorithmic work of one layer call on T tokens: the bytes the method
+    must move (the weights, codes and scales, of the distinct routed experts
+    d_layer, the router weights, x in and out) and its FP4 FLOPs (real pair
+    rows only), plus the gate/up kernel's own bytes (the weights of the
+    experts d_gate_up it streamed, quantized x in, its output) and FLOPs."""
+    b13, b2 = per_expert_bytes(w)
+    xbytes = T * w.H * (2 if x_bf16 else 4)
+    P = T * w.top_k
+    if int8:
+        g1_bytes = d_gate_up * b13 + T * 2 * w.H + P * w.I * 4
+    else:
+        g1_bytes = d_gate_up * b13 + T * w.H // 2 + T * w.H // 32 + P * (w.I // 2 + w.I // 32)
+    return {"layer_bytes": d_layer * (b13 + b2) + w.E * w.H * 4 + xbytes + T * w.H * 4,
+            "layer_flops": 2.0 * P * (w.H * 2 * w.I + w.I * w.H),
+            "gate_up_bytes": g1_bytes, "gate_up_flops": 2.0 * P * w.H * 2 * w.I}
+
+
 def graph_time(fn, reps: int, torch, sleep_ms: float = 20.0) -> float:
     """ms per replay of fn() captured into one HIP graph (after a warm-up call
     on a side stream), replayed `reps` times back to back behind a bounded GPU
@@ -200,17 +218,9 @@ def run_workload(name: str, steps: int, warmup: int, rot: int, torch, B, S, SD, 
         max_load.append(int(np.bincount(a.ravel(), minlength=w.E).max()))
     d_avg = float(np.mean([distinct[i % rot] for i in range(steps)]))
     d_sampled = float(np.mean([distinct[i % rot] for i in sampled]))
-    b13, b2 = per_expert_bytes(w)
-    xbytes = T * w.H * (2 if w.x_dtype == S.X_BF16 else 4)
-    P = T * w.top_k
-    layer_bytes = d_avg * (b13 + b2) + w.E * w.H * 4 + xbytes + T * w.H * 4
-    # gate/up kernel: weights of the routed experts + quantized x in + its output
-    if w.act_mode == S.ACT_INT8:
-        g1_bytes = d_sampled * b13 + T * 2 * w.H + P * w.I * 4
-    else:
-        g1_bytes = d_sampled * b13 + T * w.H // 2 + T * w.H // 32 + P * (w.I // 2 + w.I // 32)
-    g1_flops = 2.0 * P * w.H * 2 * w.I
-    layer_flops = 2.0 * P * (w.H * 2 * w.I + w.I * w.H)
+    acc = layer_accounting(w, T, d_avg, d_sampled, w.x_dtype == S.X_BF16, w.act_mode == S.ACT_INT8)
+    layer_bytes, layer_flops = acc["layer_bytes"], acc["layer_flops"]
+    g1_bytes, g1_flops = acc["gate_up_bytes"], acc["gate_up_flops"]
     ms_step = total_ms / steps
     return {
         "workload": name, "T": T, "steps": steps, "rot": rot, "host_enqueue_ms": host_s * 1e3,
